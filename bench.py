@@ -1,0 +1,168 @@
+#!/usr/bin/env python3
+"""Throughput of the paged MLA verify hot path on one MI355X.
+
+One step = plan (row lengths + sub-page tables) -> split-K attention partials
+-> segment + shard LSE merge, over one batch of the workload, inputs resident
+in HBM. The KV cache is rotated over several copies (more than the 256 MB
+Infinity Cache holds) so that no step re-reads the previous step's KV from
+cache. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload verify_dcp8]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA verify attention KV GB/s (% of HBM peak) + verify rows/sec at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="verify_dcp8")
+    ap.add_argument("--nseg", type=int, default=None)
+    ap.add_argument("--kv-copies", type=int, default=0,
+                    help="KV copies to rotate over (0: enough for > 512 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, target_s):
+    """Time the fp64 oracle on a bounded sample of whole requests."""
+    import oracle as orc
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    order = list(range(inp["N"]))
+    done, t_total, kv_bytes, rows = [], 0.0, 0, 0
+    bpt = wl.kv_bytes_per_token(inp["kv_dtype"])
+    for i in order:
+        t0 = time.perf_counter()
+        orc.verify_reference(inp, [i])
+        t_total += time.perf_counter() - t0
+        done.append(i)
+        kv_bytes += int(inp["seq_lens"][i]) * bpt
+        rows += int(inp["qlens"][i])
+        if t_total >= target_s:
+            break
+    return {
+        "value": kv_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {inp['N']} requests (first ones; {rows} verify rows, "
+                  f"{kv_bytes / 1e6:.1f} MB of KV) in {t_total:.1f} s; rows/s "
+                  f"{rows / t_total:.3g}; host cpus {os.cpu_count()}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as wl
+    import mla_paged_decode_verify_amd as mla
+
+    inp = wl.make_workload(args.workload, 0)
+    nseg = inp["nseg"] if args.nseg is None else args.nseg
+    dev = wl.to_device(inp)
+    kv_bytes = wl.algorithmic_kv_bytes(inp)
+    flops = wl.algorithmic_flops(inp)
+    kv_dev_bytes = dev["kv"].numel() * dev["kv"].element_size()
+    copies = args.kv_copies or (-(-(512 << 20) // kv_dev_bytes) + 1)
+    kvs = [dev["kv"]] + [dev["kv"].clone() for _ in range(copies - 1)]
+    R, H, W = inp["R"], inp["H"], inp["W"]
+
+    # preallocated outputs (the library allocates nothing)
+    page_size = mla.mla_subpage_size(inp["block_size"])
+    ptw = mla.mla_pt_width(inp["max_kv_seq_len"], page_size)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    plan_bufs = dict(row_lens=torch.empty((W, R), **i32),
+                     page_table=torch.empty((W, R, ptw), **i32),
+                     qo_indptr=torch.empty((R + 1,), **i32), err_flag=torch.empty((1,), **i32))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    parts = (torch.empty((W, R, H, nseg, 512), **f32), torch.empty((W, R, H, nseg), **f32),
+             torch.empty((W, R, H, nseg), **f32))
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, H), **f32)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(k, events=None):
+        e = events
+        if e: e[0].record()
+        plan = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], R, W, dev["block_table"],
+                                   dev["num_blocks"], inp["block_size"], inp["max_kv_seq_len"],
+                                   **plan_bufs)
+        if e: e[1].record()
+        mla.mla_verify_attn(dev["q"], kvs[k % len(kvs)], plan["row_lens"], plan["page_table"],
+                            dev["q_start"], page_size=page_size, max_qlen=dev["max_qlen"],
+                            nseg=nseg, sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                            segm_out=parts[0], segm_max=parts[1], segm_expsum=parts[2])
+        if e: e[2].record()
+        mla.mla_lse_merge(*parts, plan["row_lens"], dev["q_start"], page_size=page_size, H=H,
+                          nseg=nseg, out=out, lse=lse)
+        if e: e[3].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if int(plan_bufs["err_flag"].item()) != 0:
+        raise SystemExit(f"plan reported errors: {int(plan_bufs['err_flag'].item())}")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan_ms = np.mean([e[0].elapsed_time(e[1]) for e in ev])
+    attn_ms = np.mean([e[1].elapsed_time(e[2]) for e in ev])
+    merge_ms = np.mean([e[2].elapsed_time(e[3]) for e in ev])
+    ms_step = wall * 1e3 / args.steps
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if inp["kv_dtype"] == "bf16" else "fp8e4m3-kv/bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp["N"], "heads": H,
+                   "qlen": int(np.max(inp["qlens"])), "rows": R, "shards": W,
+                   "block_size": inp["block_size"], "page_size": page_size, "nseg": nseg,
+                   "kv_dtype": inp["kv_dtype"], "sum_seq_len": int(inp["seq_lens"].sum()),
+                   "kv_copies": len(kvs)},
+        "rows_per_s": round(R / (ms_step * 1e-3), 1),
+        "hbm_frac": round(kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_us": {"plan": round(plan_ms * 1e3, 2), "attn": round(attn_ms * 1e3, 2),
+                      "merge": round(merge_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "attn_kernel",
+                     "bytes_per_launch": kv_bytes, "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

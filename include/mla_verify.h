@@ -1,0 +1,194 @@
+/*
+ * mla_verify.h -- C ABI of the MI355X (gfx950) paged MLA decode / causal
+ * multi-token verify path over a round-robin context-sharded KV cache.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [V51705] prhub digest of vLLM PR #51705, "ROCm AITER MLA supports causal
+ *            multi-token speculative verify under DCP"
+ *   [S34432] prhub report of SGLang PR #34432, "[AMD][DCP 1/N] add dcp support
+ *            for aiter backend"
+ *   [V51011] prhub digest of vLLM PR #51011, "fix silent wrong decode for fp8
+ *            KV in ROCm AITER MLA"
+ *
+ * Notation. N requests; request i has S_i cached tokens (its Q_i verify tokens
+ * included, all already written to the cache) and Q_i >= 1 verify rows. Rows
+ * are request-major: row rho = q_start[i] + t, t in [0, Q_i), R = q_start[N].
+ * W shards hold each sequence round-robin with interleave 1: global position p
+ * lives on shard p % W at local index p / W. H heads. Head dim 576 = 512
+ * latent + 64 rope; V is the 512 latent values of the same cache entry.
+ *
+ * Conventions for every call below.
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays,
+ *     allocated and owned by the caller. The library allocates no device
+ *     memory and keeps no state except a thread-local error string.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; 0 = the
+ *     default stream). Nothing synchronises.
+ *   - Scalar arguments are validated on the host before anything is
+ *     launched: a bad value returns MLA_ERR_INVALID (or MLA_ERR_UNSUPPORTED
+ *     for a layout the library does not implement) and launches nothing;
+ *     mla_last_error() then describes it. A failed launch returns
+ *     MLA_ERR_HIP. Device data the host cannot see without a sync is checked
+ *     by mla_verify_plan on the device (see err_flag).
+ */
+#ifndef MLA_VERIFY_H_
+#define MLA_VERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID = 1,     /* bad argument; nothing was launched            */
+  MLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. interleave>1) */
+  MLA_ERR_HIP = 3          /* a HIP launch failed                           */
+} mla_status_t;
+
+typedef enum {
+  MLA_KV_BF16 = 0,     /* bf16 cache entries, 1152 bytes per token           */
+  MLA_KV_FP8_E4M3 = 1  /* OCP e4m3fn codes, 576 bytes per token, real value =
+                          code * kv_scale (one per-tensor float scale)       */
+} mla_kv_dtype_t;
+
+#define MLA_HEAD_DIM 576
+#define MLA_V_DIM 512
+
+/* Device error bits written to *err_flag by mla_verify_plan. A request with
+ * any of these problems gets row length 0 on every shard and an all -1
+ * sub-page table, so later calls never read outside the caller's buffers. */
+#define MLA_PLAN_ERR_QLEN 1u    /* Q_i < 1, S_i < Q_i, or q_start not monotone  */
+#define MLA_PLAN_ERR_BOUND 2u   /* ceil(S_i / W) > max_kv_seq_len               */
+#define MLA_PLAN_ERR_BLOCKS 4u  /* request needs more than max_blocks blocks, or
+                                   a block id it uses is outside [0,num_blocks) */
+#define MLA_PLAN_ERR_ROWS 8u    /* q_start[N] != R                              */
+
+/*
+ * Sub-page size for a physical block size: the largest power of two that
+ * divides block_size, capped at 128 ([V51705] Implementation breakdown item 3,
+ * `_segmented_mla_page_size` snippet). It is the tile unit of the split-K
+ * partition. Returns -1 if block_size <= 0. Host only.
+ */
+int32_t mla_subpage_size(int32_t block_size);
+
+/*
+ * Width of the per-row sub-page table: ceil(max_kv_seq_len / page_size).
+ * max_kv_seq_len is the kernel-visible bound on any shard-local length
+ * ([V51705] `AiterMLADCPVerifyMetadata.max_kv_seq_len`); a fixed configured
+ * bound keeps the table shape stable between calls. Returns -1 on bad input.
+ */
+int32_t mla_pt_width(int32_t max_kv_seq_len, int32_t page_size);
+
+/*
+ * Bytes of the three split-K partial buffers for W shards, R rows, H heads and
+ * nseg segments: segm_out (W*R*H*nseg*512 floats) + segm_max and segm_expsum
+ * (W*R*H*nseg floats each). Returns 0 on bad input. Host only.
+ */
+size_t mla_verify_workspace_bytes(int32_t W, int32_t R, int32_t H, int32_t nseg);
+
+/*
+ * Plan: rank-local row lengths and sub-page tables for every verify row on
+ * every shard ([V51705] Implementation breakdown items 2-3 and the
+ * `_build_dcp_verify_row_view` / `AiterMLADCPVerifyMetadata` snippets).
+ * Built once per forward, shared by every layer.
+ *
+ *   seq_lens    [N]   int32  S_i
+ *   q_start     [N+1] int32  row offsets (q_start[0] = 0, q_start[N] = R)
+ *   interleave  must be 1 (round-robin one token at a time); any other value
+ *               returns MLA_ERR_UNSUPPORTED ([V51705] item 1: only
+ *               interleave 1 has a verified per-row window)
+ *   block_table [N, max_blocks] int32 physical block ids, one table shared by
+ *               every shard's pool; local token j of request i is in block
+ *               block_table[i][j / block_size] at offset j % block_size
+ *   num_blocks  blocks in each shard's pool (ids must be < num_blocks)
+ *   page_size   must equal mla_subpage_size(block_size) (carried explicitly,
+ *               never re-derived from a cache shape: [V51705] snippet)
+ *   pt_width    must be >= mla_pt_width(max_kv_seq_len, page_size)
+ * Outputs (device):
+ *   row_lens    [W, R] int32  L[r][rho] = #{ p < w : p % W == r } with the
+ *               window w = S_i - Q_i + 1 + t (row t sees global positions
+ *               [0, S_i - Q_i + t], its own token included)
+ *   page_table  [W, R, pt_width] int32 sub-page ids; entry k < ceil(L/P) is
+ *               block_table[i][k*P / B] * (B/P) + (k*P % B) / P, the rest -1
+ *   qo_indptr   [R+1] int32 = 0..R (one query per row); may be NULL
+ *   err_flag    [1] uint32, may be NULL: set to the OR of MLA_PLAN_ERR_* bits
+ *               (0 when every request is valid)
+ */
+mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
+                             const int32_t* q_start, int32_t R, int32_t W,
+                             int32_t interleave, const int32_t* block_table,
+                             int32_t max_blocks, int64_t num_blocks,
+                             int32_t block_size, int32_t page_size,
+                             int32_t max_kv_seq_len, int32_t pt_width,
+                             int32_t* row_lens, int32_t* page_table,
+                             int32_t* qo_indptr, uint32_t* err_flag,
+                             void* stream);
+
+/*
+ * Split-K segmented attention partials for every (shard, row, head, segment)
+ * ([V51705] Implementation breakdown item 4 and the merge snippet).
+ *
+ *   q          [R, H, 576] bf16 queries (RoPE already applied)
+ *   kv         [W, num_blocks, block_size, 576] cache: one pool per shard,
+ *              elements bf16 or e4m3fn per kv_dtype; 16-byte aligned
+ *   kv_scale   fp8 descale (real = code * kv_scale); ignored for bf16
+ *   sm_scale   softmax scale applied to <q, k> (e.g. 1/sqrt(576))
+ *   row_lens, page_table, pt_width, page_size: from mla_verify_plan
+ *   q_start    [N+1] as given to the plan; max_qlen >= every Q_i
+ *   nseg       segments per (request, shard) group. Partition (a reading of
+ *              the pages' tiles_per_segment = ceil(len/(nseg*TILE))): with Lg
+ *              the group's longest row (its last), T = ceil(Lg/(nseg*P)) and
+ *              segment s covers local tokens [s*T*P, (s+1)*T*P), clipped to
+ *              each row's own length.
+ * Outputs (device, fp32), index e = ((r*R + rho)*H + h)*nseg + s:
+ *   segm_max[e]    max over the segment of sm_scale*<q,k>*log2(e)  (base 2)
+ *   segm_expsum[e] sum over the segment of 2^(score2 - segm_max[e])
+ *   segm_out[e*512 + d] sum of 2^(score2 - segm_max[e]) * v[d]  (unnormalised)
+ * Only segments with s*T*P < Lg are written; entries of other segments are
+ * left untouched (mla_lse_merge does not read them). A row with no token in
+ * a written segment gets (-inf, 0, 0).
+ */
+mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
+                             int32_t block_size, int32_t page_size,
+                             mla_kv_dtype_t kv_dtype, float kv_scale,
+                             float sm_scale, const int32_t* row_lens,
+                             const int32_t* page_table, int32_t pt_width,
+                             const int32_t* q_start, int32_t N, int32_t R,
+                             int32_t H, int32_t W, int32_t max_qlen,
+                             int32_t nseg, float* segm_out, float* segm_max,
+                             float* segm_expsum, void* stream);
+
+/*
+ * Segment merge then shard merge ([V51705] merge snippet and Implementation
+ * breakdown item 4; [S34432] review item 4 for the natural-log convention).
+ * Per shard r, over its active segments (s*T*P < that row's length):
+ *   M = max m2_s, E = sum e_s 2^(m2_s - M), o_r = sum O_s 2^(m2_s - M) / E,
+ *   lse_r = ln2 * (M + log2 E)   (natural log; -inf and o_r = 0 if none),
+ * o_r rounded to bf16 as a shard would send it. Then across shards:
+ *   lse = ln sum_r exp(lse_r), out = sum_r exp(lse_r - lse) * o_r  -> bf16.
+ * Never produces NaN from empty shards or segments.
+ *
+ *   segm_*       from mla_verify_attn with the same R, H, W, nseg
+ *   row_lens, q_start, N, page_size: as given to mla_verify_attn
+ *   shard_out    [W, R, H, 512] bf16, may be NULL   (per-shard o_r)
+ *   shard_lse    [W, R, H] fp32, may be NULL        (per-shard lse_r)
+ *   out          [R, H, 512] bf16
+ *   lse          [R, H] fp32, natural log, unpadded in heads
+ */
+mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
+                           const float* segm_expsum, const int32_t* row_lens,
+                           const int32_t* q_start, int32_t N, int32_t page_size,
+                           int32_t R, int32_t H, int32_t W, int32_t nseg,
+                           void* shard_out, float* shard_lse, void* out,
+                           float* lse, void* stream);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H_ */

@@ -1,0 +1,229 @@
+"""MI355X (gfx950) paged MLA decode / causal multi-token verify over a
+round-robin context-sharded KV cache.
+
+Thin binding over the C ABI in include/mla_verify.h (libmla_verify.so): the
+functions below only check and marshal torch tensors (device pointers, the
+current HIP stream) and allocate outputs the caller did not pass. Every step
+of the computation runs in the HIP kernels of the library.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (MLA_ERR_HIP, MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED,  # noqa: F401
+                   MLA_KV_BF16, MLA_KV_FP8_E4M3, MLA_OK, MLA_PLAN_ERR_BLOCKS,
+                   MLA_PLAN_ERR_BOUND, MLA_PLAN_ERR_QLEN, MLA_PLAN_ERR_ROWS)
+
+HEAD_DIM = 576
+V_DIM = 512
+LIB_PATH = _lib.LIB_PATH
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def mla_last_error() -> str:
+    return (_lib.lib.mla_last_error() or b"").decode()
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MlaError(status, mla_last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def mla_subpage_size(block_size: int) -> int:
+    return int(_lib.lib.mla_subpage_size(int(block_size)))
+
+
+def mla_pt_width(max_kv_seq_len: int, page_size: int) -> int:
+    return int(_lib.lib.mla_pt_width(int(max_kv_seq_len), int(page_size)))
+
+
+def mla_verify_workspace_bytes(W: int, R: int, H: int, nseg: int) -> int:
+    return int(_lib.lib.mla_verify_workspace_bytes(int(W), int(R), int(H), int(nseg)))
+
+
+def mla_verify_plan(seq_lens, q_start, R, W, block_table, num_blocks, block_size,
+                    max_kv_seq_len, *, page_size=None, pt_width=None, interleave=1,
+                    row_lens=None, page_table=None, qo_indptr=None, err_flag=None,
+                    stream=None):
+    """Row lengths [W, R], sub-page table [W, R, pt_width], qo_indptr [R+1] and
+    the device error word (int32 view of the uint32 MLA_PLAN_ERR_* bits).
+    seq_lens [N], q_start [N+1] and block_table [N, max_blocks] are int32
+    device tensors; R = q_start[N] is passed by the caller (no device read)."""
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(q_start, torch.int32, "q_start")
+    _dev(block_table, torch.int32, "block_table")
+    N = seq_lens.shape[0]
+    if q_start.shape != (N + 1,):
+        raise ValueError("q_start must have N+1 entries")
+    if block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("block_table must be [N, max_blocks]")
+    if page_size is None:
+        page_size = mla_subpage_size(block_size)
+    if pt_width is None:
+        pt_width = mla_pt_width(max_kv_seq_len, page_size)
+    dev = seq_lens.device
+    if row_lens is None:
+        row_lens = torch.empty((W, R), dtype=torch.int32, device=dev)
+    if page_table is None:
+        page_table = torch.empty((W, R, max(pt_width, 0)), dtype=torch.int32, device=dev)
+    if qo_indptr is None:
+        qo_indptr = torch.empty((R + 1,), dtype=torch.int32, device=dev)
+    if err_flag is None:
+        err_flag = torch.empty((1,), dtype=torch.int32, device=dev)
+    for t, n in ((row_lens, "row_lens"), (page_table, "page_table"),
+                 (qo_indptr, "qo_indptr"), (err_flag, "err_flag")):
+        _dev(t, torch.int32, n)
+    if tuple(row_lens.shape) != (W, R) or tuple(page_table.shape) != (W, R, pt_width) \
+            or qo_indptr.numel() != R + 1:
+        raise ValueError("row_lens / page_table shape mismatch")
+    _check(_lib.lib.mla_verify_plan(
+        N, _ptr(seq_lens), _ptr(q_start), int(R), int(W), interleave, _ptr(block_table),
+        block_table.shape[1], int(num_blocks), block_size, page_size, max_kv_seq_len,
+        pt_width, _ptr(row_lens), _ptr(page_table), _ptr(qo_indptr), _ptr(err_flag),
+        _stream(stream)))
+    return {"row_lens": row_lens, "page_table": page_table, "qo_indptr": qo_indptr,
+            "err_flag": err_flag, "page_size": page_size, "pt_width": pt_width, "R": R}
+
+
+def _kv_dtype(kv):
+    if kv.dtype == torch.bfloat16:
+        return MLA_KV_BF16
+    if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MLA_KV_FP8_E4M3
+    raise TypeError(f"kv must be bfloat16 or e4m3fn (uint8) codes, got {kv.dtype}")
+
+
+def mla_verify_attn(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen,
+                    nseg, sm_scale, kv_scale=1.0, segm_out=None, segm_max=None,
+                    segm_expsum=None, stream=None):
+    """Split-K partials. q [R, H, 576] bf16; kv [W, num_blocks, block_size, 576]
+    bf16 or e4m3fn codes. Returns (segm_out, segm_max, segm_expsum)."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(kv, None, "kv")
+    kvd = _kv_dtype(kv)
+    _dev(row_lens, torch.int32, "row_lens")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(q_start, torch.int32, "q_start")
+    R, H, D = q.shape
+    W, num_blocks, block_size, D2 = kv.shape
+    if D != HEAD_DIM or D2 != HEAD_DIM:
+        raise ValueError("head dim must be 576")
+    if tuple(row_lens.shape) != (W, R) or page_table.shape[:2] != (W, R):
+        raise ValueError("plan tensors do not match q / kv")
+    N = q_start.shape[0] - 1
+    dev = q.device
+    if segm_out is None:
+        segm_out = torch.empty((W, R, H, nseg, V_DIM), dtype=torch.float32, device=dev)
+    if segm_max is None:
+        segm_max = torch.empty((W, R, H, nseg), dtype=torch.float32, device=dev)
+    if segm_expsum is None:
+        segm_expsum = torch.empty((W, R, H, nseg), dtype=torch.float32, device=dev)
+    for t, n in ((segm_out, "segm_out"), (segm_max, "segm_max"), (segm_expsum, "segm_expsum")):
+        _dev(t, torch.float32, n)
+    if segm_out.numel() != W * R * H * nseg * V_DIM or segm_max.numel() != W * R * H * nseg \
+            or segm_expsum.numel() != W * R * H * nseg:
+        raise ValueError("partial buffers have the wrong size")
+    _check(_lib.lib.mla_verify_attn(
+        _ptr(q), _ptr(kv), num_blocks, block_size, page_size, kvd, float(kv_scale),
+        float(sm_scale), _ptr(row_lens), _ptr(page_table), page_table.shape[2],
+        _ptr(q_start), N, R, H, W, int(max_qlen), int(nseg), _ptr(segm_out),
+        _ptr(segm_max), _ptr(segm_expsum), _stream(stream)))
+    return segm_out, segm_max, segm_expsum
+
+
+def mla_lse_merge(segm_out, segm_max, segm_expsum, row_lens, q_start, *, page_size,
+                  H, nseg, out=None, lse=None, shard_out=None, shard_lse=None,
+                  want_shards=False, stream=None):
+    """Segment merge + shard LSE merge. Returns (out [R,H,512] bf16,
+    lse [R,H] fp32, shard_out [W,R,H,512] bf16 or None, shard_lse or None)."""
+    _dev(row_lens, torch.int32, "row_lens")
+    _dev(q_start, torch.int32, "q_start")
+    for t, n in ((segm_out, "segm_out"), (segm_max, "segm_max"), (segm_expsum, "segm_expsum")):
+        _dev(t, torch.float32, n)
+    W, R = row_lens.shape
+    N = q_start.shape[0] - 1
+    dev = row_lens.device
+    if segm_out.numel() != W * R * H * nseg * V_DIM or segm_max.numel() != W * R * H * nseg:
+        raise ValueError("partial buffers do not match W, R, H, nseg")
+    if out is None:
+        out = torch.empty((R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    if want_shards and shard_out is None:
+        shard_out = torch.empty((W, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if want_shards and shard_lse is None:
+        shard_lse = torch.empty((W, R, H), dtype=torch.float32, device=dev)
+    _dev(out, torch.bfloat16, "out")
+    _dev(lse, torch.float32, "lse")
+    if out.numel() != R * H * V_DIM or lse.numel() != R * H:
+        raise ValueError("out / lse have the wrong size")
+    if shard_out is not None:
+        _dev(shard_out, torch.bfloat16, "shard_out")
+        if shard_out.numel() != W * R * H * V_DIM:
+            raise ValueError("shard_out has the wrong size")
+    if shard_lse is not None:
+        _dev(shard_lse, torch.float32, "shard_lse")
+        if shard_lse.numel() != W * R * H:
+            raise ValueError("shard_lse has the wrong size")
+    _check(_lib.lib.mla_lse_merge(
+        _ptr(segm_out), _ptr(segm_max), _ptr(segm_expsum), _ptr(row_lens), _ptr(q_start),
+        N, page_size, R, H, W, nseg, _ptr(shard_out), _ptr(shard_lse), _ptr(out), _ptr(lse),
+        _stream(stream)))
+    return out, lse, shard_out, shard_lse
+
+
+def mla_verify_forward(dev, *, nseg=1, plan=None, partials=None, out=None, lse=None,
+                       want_shards=False, stream=None):
+    """plan -> attention partials -> merge for a dict of device tensors
+    (keys: q, kv, seq_lens, q_start, block_table, num_blocks, block_size, R, W,
+    max_kv_seq_len, max_qlen, sm_scale, kv_scale). Returns a dict with the plan,
+    the partials and (out, lse[, shard_out, shard_lse])."""
+    if plan is None:
+        plan = mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
+                               dev["block_table"], dev["num_blocks"], dev["block_size"],
+                               dev["max_kv_seq_len"], stream=stream)
+    kw = {}
+    if partials is not None:
+        kw = dict(segm_out=partials[0], segm_max=partials[1], segm_expsum=partials[2])
+    parts = mla_verify_attn(dev["q"], dev["kv"], plan["row_lens"], plan["page_table"],
+                            dev["q_start"], page_size=plan["page_size"],
+                            max_qlen=dev["max_qlen"], nseg=nseg, sm_scale=dev["sm_scale"],
+                            kv_scale=dev["kv_scale"], stream=stream, **kw)
+    o, l, so, sl = mla_lse_merge(*parts, plan["row_lens"], dev["q_start"],
+                                 page_size=plan["page_size"], H=dev["q"].shape[1], nseg=nseg,
+                                 out=out, lse=lse, want_shards=want_shards, stream=stream)
+    return {"plan": plan, "partials": parts, "out": o, "lse": l, "shard_out": so,
+            "shard_lse": sl}
+
+
+__all__ = [
+    "mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes", "mla_verify_plan",
+    "mla_verify_attn", "mla_lse_merge", "mla_last_error", "mla_verify_forward", "MlaError", "HEAD_DIM", "V_DIM",
+]

@@ -1,0 +1,56 @@
+"""ctypes loader for libmla_verify.so with the C prototypes of include/mla_verify.h.
+
+There is no fallback: if the library is not built, importing fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_verify.so")
+
+MLA_OK, MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
+MLA_KV_BF16, MLA_KV_FP8_E4M3 = 0, 1
+MLA_PLAN_ERR_QLEN, MLA_PLAN_ERR_BOUND, MLA_PLAN_ERR_BLOCKS, MLA_PLAN_ERR_ROWS = 1, 2, 4, 8
+
+EXPORTED = {
+    # name: (restype, argtypes)
+    "mla_subpage_size": (ctypes.c_int32, [ctypes.c_int32]),
+    "mla_pt_width": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
+    "mla_verify_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 4),
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_verify_plan": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "mla_verify_attn": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p]),
+    "mla_lse_merge": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
+}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m mla_paged_decode_verify_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTED.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = load()

@@ -1,0 +1,191 @@
+// Host side of the C ABI: argument validation, then kernel launches.
+// Every check runs before anything is enqueued, so a rejected call leaves the
+// stream and the caller's buffers untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status_t fail(mla_status_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+mla_status_t ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+mla_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t subpage_size(int32_t block_size) {
+  if (block_size <= 0) return -1;
+  int32_t p = 1;
+  int32_t rest = block_size;
+  while ((rest & 1) == 0 && p < 128) {
+    rest >>= 1;
+    p <<= 1;
+  }
+  return p;
+}
+
+int log2_exact(int32_t p) {
+  int k = 0;
+  while ((1 << k) < p) ++k;
+  return k;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_subpage_size(int32_t block_size) { return subpage_size(block_size); }
+
+int32_t mla_pt_width(int32_t max_kv_seq_len, int32_t page_size) {
+  if (max_kv_seq_len < 0 || page_size <= 0) return -1;
+  return (int32_t)(((int64_t)max_kv_seq_len + page_size - 1) / page_size);
+}
+
+size_t mla_verify_workspace_bytes(int32_t W, int32_t R, int32_t H, int32_t nseg) {
+  if (W < 1 || R < 0 || H < 1 || nseg < 1) return 0;
+  const size_t cells = (size_t)W * (size_t)R * (size_t)H * (size_t)nseg;
+  return cells * (mla::kVDim + 2) * sizeof(float);
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens, const int32_t* q_start,
+                             int32_t R, int32_t W, int32_t interleave,
+                             const int32_t* block_table, int32_t max_blocks,
+                             int64_t num_blocks, int32_t block_size, int32_t page_size,
+                             int32_t max_kv_seq_len, int32_t pt_width, int32_t* row_lens,
+                             int32_t* page_table, int32_t* qo_indptr, uint32_t* err_flag,
+                             void* stream) {
+  if (N < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: N must be >= 1 (got %d)", N);
+  if (R < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: R must be >= 1 (got %d)", R);
+  if (W < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: W must be >= 1 (got %d)", W);
+  if (interleave != 1)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_verify_plan: only round-robin interleave 1 is supported (got %d)",
+                interleave);
+  if (block_size <= 0)
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: block_size must be > 0 (got %d)", block_size);
+  if (page_size != subpage_size(block_size))
+    return fail(MLA_ERR_INVALID,
+                "mla_verify_plan: page_size %d != sub-page size %d of block_size %d",
+                page_size, subpage_size(block_size), block_size);
+  if (max_blocks < 1)
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: max_blocks must be >= 1 (got %d)", max_blocks);
+  if (num_blocks < 1)
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: num_blocks must be >= 1");
+  if (num_blocks * (int64_t)(block_size / page_size) > 0x7FFFFFFFLL)
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: too many sub-pages for int32 ids");
+  if (max_kv_seq_len < 0)
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: max_kv_seq_len must be >= 0");
+  if (pt_width < mla_pt_width(max_kv_seq_len, page_size) || pt_width < 0)
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: pt_width %d < ceil(max_kv_seq_len/page_size) = %d",
+                pt_width, mla_pt_width(max_kv_seq_len, page_size));
+  if ((int64_t)W * R * (int64_t)(pt_width > 0 ? pt_width : 1) > (1LL << 40))
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: page table too large");
+  if (!seq_lens || !q_start || !block_table || !row_lens || (pt_width > 0 && !page_table))
+    return fail(MLA_ERR_INVALID, "mla_verify_plan: null tensor argument");
+
+  mla::PlanArgs a{};
+  a.N = N; a.R = R; a.W = W;
+  a.seq_lens = seq_lens; a.q_start = q_start; a.block_table = block_table;
+  a.max_blocks = max_blocks; a.num_blocks = num_blocks;
+  a.block_size = block_size; a.page_size = page_size;
+  a.max_kv_seq_len = max_kv_seq_len; a.pt_width = pt_width;
+  a.row_lens = row_lens; a.page_table = page_table; a.qo_indptr = qo_indptr;
+  a.err_flag = err_flag;
+  return hip_status(mla::launch_plan(a, (hipStream_t)stream), "mla_verify_plan launch");
+}
+
+mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
+                             int32_t block_size, int32_t page_size, mla_kv_dtype_t kv_dtype,
+                             float kv_scale, float sm_scale, const int32_t* row_lens,
+                             const int32_t* page_table, int32_t pt_width,
+                             const int32_t* q_start, int32_t N, int32_t R, int32_t H,
+                             int32_t W, int32_t max_qlen, int32_t nseg, float* segm_out,
+                             float* segm_max, float* segm_expsum, void* stream) {
+  if (N < 1 || R < 1 || H < 1 || W < 1)
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: N, R, H, W must be >= 1 (got %d, %d, %d, %d)",
+                N, R, H, W);
+  if (nseg < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: nseg must be >= 1 (got %d)", nseg);
+  if (max_qlen < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: max_qlen must be >= 1");
+  if (block_size <= 0 || page_size != subpage_size(block_size))
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: page_size %d does not match block_size %d",
+                page_size, block_size);
+  if (num_blocks < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: num_blocks must be >= 1");
+  if (pt_width < 0) return fail(MLA_ERR_INVALID, "mla_verify_attn: pt_width must be >= 0");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_verify_attn: unknown kv_dtype %d", (int)kv_dtype);
+  if (!std::isfinite(sm_scale) || (kv_dtype == MLA_KV_FP8_E4M3 && !std::isfinite(kv_scale)))
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: non-finite scale");
+  if (!q || !kv || !row_lens || !q_start || !segm_out || !segm_max || !segm_expsum ||
+      (pt_width > 0 && !page_table))
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: null tensor argument");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(segm_out))
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: q, kv and segm_out must be 16-byte aligned");
+  const int64_t mblocks = ((int64_t)max_qlen * H + mla::kAttnRows - 1) / mla::kAttnRows;
+  if ((int64_t)N * W * nseg * mblocks > 0x7FFFFFFFLL)
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: grid too large");
+
+  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  mla::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.pool_tokens = num_blocks * block_size;
+  a.num_subpages = num_blocks * (block_size / page_size);
+  a.page_size = page_size;
+  a.page_shift = log2_exact(page_size);
+  a.row_lens = row_lens; a.page_table = page_table; a.pt_width = pt_width;
+  a.q_start = q_start; a.N = N; a.R = R; a.H = H; a.W = W; a.nseg = nseg;
+  a.mblocks = (int32_t)mblocks;
+  const double log2e = 1.4426950408889634;
+  a.qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)kv_scale : 1.0) * log2e);
+  a.v_scale = fp8 ? kv_scale : 1.0f;
+  a.segm_out = segm_out; a.segm_max = segm_max; a.segm_expsum = segm_expsum;
+  return hip_status(mla::launch_attn(a, fp8, (hipStream_t)stream), "mla_verify_attn launch");
+}
+
+mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
+                           const float* segm_expsum, const int32_t* row_lens,
+                           const int32_t* q_start, int32_t N, int32_t page_size, int32_t R,
+                           int32_t H, int32_t W, int32_t nseg, void* shard_out,
+                           float* shard_lse, void* out, float* lse, void* stream) {
+  if (N < 1 || R < 1 || H < 1 || W < 1)
+    return fail(MLA_ERR_INVALID, "mla_lse_merge: N, R, H, W must be >= 1");
+  if (nseg < 1) return fail(MLA_ERR_INVALID, "mla_lse_merge: nseg must be >= 1");
+  if (page_size <= 0 || (page_size & (page_size - 1)) != 0 || page_size > 128)
+    return fail(MLA_ERR_INVALID, "mla_lse_merge: page_size must be a power of two <= 128");
+  if (!segm_out || !segm_max || !segm_expsum || !row_lens || !q_start || !out || !lse)
+    return fail(MLA_ERR_INVALID, "mla_lse_merge: null tensor argument");
+  if (!aligned16(segm_out) || !aligned16(out) || (shard_out && !aligned16(shard_out)))
+    return fail(MLA_ERR_INVALID, "mla_lse_merge: segm_out, out, shard_out must be 16-byte aligned");
+  mla::MergeArgs a{};
+  a.segm_out = segm_out; a.segm_max = segm_max; a.segm_expsum = segm_expsum;
+  a.row_lens = row_lens; a.q_start = q_start; a.N = N; a.page_size = page_size;
+  a.R = R; a.H = H; a.W = W; a.nseg = nseg;
+  a.shard_out = static_cast<uint16_t*>(shard_out); a.shard_lse = shard_lse;
+  a.out = static_cast<uint16_t*>(out); a.lse = lse;
+  return hip_status(mla::launch_merge(a, (hipStream_t)stream), "mla_lse_merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_verify.h"
+
+namespace mla {
+
+constexpr int kHeadDim = 576;  // 512 latent + 64 rope
+constexpr int kVDim = 512;
+
+struct PlanArgs {
+  int32_t N, R, W;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int64_t num_blocks;
+  int32_t block_size, page_size, max_kv_seq_len, pt_width;
+  int32_t* row_lens;
+  int32_t* page_table;
+  int32_t* qo_indptr;
+  uint32_t* err_flag;
+};
+
+struct AttnArgs {
+  const uint16_t* q;         // [R, H, 576] bf16 bits
+  const uint8_t* kv;         // [W, num_blocks, block_size, 576] elements
+  int64_t pool_tokens;       // num_blocks * block_size (tokens per shard pool)
+  int64_t num_subpages;      // num_blocks * block_size / page_size
+  int32_t page_shift;        // log2(page_size)
+  int32_t page_size;
+  const int32_t* row_lens;   // [W, R]
+  const int32_t* page_table; // [W, R, pt_width]
+  int32_t pt_width;
+  const int32_t* q_start;    // [N+1]
+  int32_t N, R, H, W, nseg;
+  int32_t mblocks;           // ceil(max_qlen * H / rows per workgroup)
+  float qk_scale_log2;       // sm_scale * (fp8: kv_scale) * log2(e)
+  float v_scale;             // fp8: kv_scale, bf16: 1
+  float* segm_out;
+  float* segm_max;
+  float* segm_expsum;
+};
+
+struct MergeArgs {
+  const float* segm_out;
+  const float* segm_max;
+  const float* segm_expsum;
+  const int32_t* row_lens;
+  const int32_t* q_start;
+  int32_t N, page_size, R, H, W, nseg;
+  uint16_t* shard_out;  // may be null
+  float* shard_lse;     // may be null
+  uint16_t* out;
+  float* lse;
+};
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+// Rows of one attention workgroup (two groups of 32 rows).
+constexpr int kAttnRows = 64;
+
+}  // namespace mla

@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on cuda:0.
+
+Plans (row lengths, sub-page tables, qo_indptr) must match bit for bit.
+Outputs: |out - ref| <= max(1e-2 (bf16 KV) or 3e-2 (fp8 KV), 2^-7 |ref|) --
+the floor is the stated max-abs bound, the relative term the spacing of the bf16
+output format (see tests/helpers.py) -- and max-abs 1e-3 on the LSE.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as orc
+import workloads as wl
+from helpers import (TOL_LSE, TOL_OUT, compare_requests, max_err, named_workload,
+                     oracle_plan, oracle_shard_results, out_excess, run_gpu,
+                     sample_requests, say, small_spec)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+mla = pytest.importorskip("mla_paged_decode_verify_amd")
+
+
+def _check_plan(inp, got):
+    ref = oracle_plan(inp)
+    assert got["err_flag"] == 0
+    assert got["page_size"] == ref["page_size"]
+    assert np.array_equal(got["row_lens"], ref["row_lens"])
+    assert np.array_equal(got["page_table"], ref["page_table"])
+    assert np.array_equal(got["qo_indptr"], ref["qo_indptr"])
+    return ref
+
+
+# ------------------------------------------------------------ small cases ---
+
+SMALL = {
+    "decode_w1": small_spec(W=1, qlen=1, seq_range=(30, 300), block_size=16),
+    "verify_w3_b64": small_spec(),
+    "verify_w4_b16": small_spec(W=4, block_size=16, seq_range=(60, 700)),
+    "verify_w2_b256_p128": small_spec(W=2, block_size=256, seq_range=(200, 900)),
+    "verify_w8_b48_p16": small_spec(W=8, block_size=48, seq_range=(100, 1000), qlen=5),
+    "odd_block_p1": small_spec(W=2, block_size=3, seq_range=(20, 90), qlen=2, H=4),
+    "fp8_w4": small_spec(W=4, kv_dtype="fp8_e4m3", qlen=7, H=12, seq_range=(100, 600)),
+    "heads128_q8": small_spec(N=2, H=128, qlen=8, W=1, block_size=256, seq_range=(100, 300)),
+    "heads12_q7_m84": small_spec(N=3, H=12, qlen=7, W=2, seq_range=(70, 260)),
+    "ragged_q": dict(N=5, H=8, qlen_range=(1, 8), seq_range=(8, 200), block_size=32, W=3,
+                     kv_dtype="bf16", nseg=1),
+    "w_gt_s": dict(N=4, H=4, qlens=[1, 2, 3, 4], seq_lens=[1, 3, 5, 4],
+                   block_size=16, W=8, kv_dtype="bf16", nseg=1),
+    "q_equals_s": dict(N=2, H=16, qlens=[7, 1], seq_lens=[7, 1], block_size=16, W=2,
+                       kv_dtype="bf16", nseg=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("nseg", [1, 3])
+def test_small_parity_all_stages(name, nseg):
+    """Every stage against the oracle on inputs the oracle finishes in
+    seconds: plan bit-exact, split-K partials, per-shard (out, lse), final."""
+    spec = dict(SMALL[name])
+    inp = wl.make_workload(spec, seed=1)
+    say(f"case {name} nseg={nseg} S={inp['seq_lens'].tolist()} Q={inp['qlens'].tolist()}")
+    got = run_gpu(inp, nseg=nseg, want_shards=True)
+    ref = _check_plan(inp, got)
+    so, sl, parts = oracle_shard_results(inp, ref, nseg)
+    assert np.all(np.isfinite(got["out"])) and not np.any(np.isnan(got["lse"]))
+    assert out_excess(got["shard_out"], so, inp["kv_dtype"]) <= 1.0
+    assert max_err(got["shard_lse"], sl) <= TOL_LSE
+    # split-K partials on active (row, segment) pairs
+    H, W, R = inp["H"], inp["W"], inp["R"]
+    gm = got["segm_max"].reshape(W, R, H, nseg)
+    ge = got["segm_expsum"].reshape(W, R, H, nseg)
+    go = got["segm_out"].reshape(W, R, H, nseg, 512)
+    for (i, r), (m2, e, O, act) in parts.items():
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        for t in range(Q):
+            for s in np.nonzero(act[t])[0]:
+                rho = qs + t
+                assert max_err(gm[r, rho, :, s], m2[t, :, s]) <= 1e-3
+                assert np.allclose(ge[r, rho, :, s], e[t, :, s], rtol=2e-3, atol=0)
+                assert out_excess(go[r, rho, :, s] / ge[r, rho, :, s, None],
+                                  O[t, :, s] / e[t, :, s, None], inp["kv_dtype"]) <= 1.0
+    out_ref, lse_ref = orc.verify_reference(inp)
+    say(f"  max|dout|={max_err(got['out'], out_ref):.3e} max|dlse|={max_err(got['lse'], lse_ref):.3e}")
+    assert out_excess(got["out"], out_ref, inp["kv_dtype"]) <= 1.0
+    assert max_err(got["lse"], lse_ref) <= TOL_LSE
+
+
+@pytest.mark.parametrize("W,B", [(1, 16), (2, 64), (3, 48), (5, 3), (8, 256), (16, 32)])
+def test_plan_fuzz_bit_exact(W, B):
+    for seed in range(3):
+        spec = dict(N=7, H=1, qlen_range=(1, 9), seq_range=(9, 700), block_size=B, W=W,
+                    kv_dtype="bf16", nseg=1)
+        inp = wl.make_workload(spec, seed=seed)
+        dev = wl.to_device(inp)
+        p = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], W,
+                                dev["block_table"], dev["num_blocks"], B,
+                                dev["max_kv_seq_len"] + seed * 17)
+        torch.cuda.synchronize()
+        ref = orc.plan(inp["seq_lens"], inp["q_start"], W, inp["block_table"], B,
+                       inp["max_kv_seq_len"] + seed * 17)
+        assert int(p["err_flag"].item()) == 0
+        assert np.array_equal(p["row_lens"].cpu().numpy(), ref["row_lens"])
+        assert np.array_equal(p["page_table"].cpu().numpy(), ref["page_table"])
+
+
+def _plan_raw(seq_lens, qlens, W, block_table, num_blocks, B, max_kv, R=None):
+    q_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.int32), device="cuda")
+    R = int(q_start[-1]) if R is None else R
+    p = mla.mla_verify_plan(t(seq_lens), t(q_start), R, W, t(block_table), num_blocks, B, max_kv)
+    torch.cuda.synchronize()
+    return p
+
+
+def test_plan_device_error_bits():
+    bt = [[0, 1], [2, 3]]
+    ok = _plan_raw([40, 30], [2, 3], 2, bt, 4, 16, 20)
+    assert int(ok["err_flag"].item()) == 0
+    bad_q = _plan_raw([40, 2], [2, 3], 2, bt, 4, 16, 20)          # S < Q
+    assert int(bad_q["err_flag"].item()) & mla.MLA_PLAN_ERR_QLEN
+    L = bad_q["row_lens"].cpu().numpy()
+    assert np.all(L[:, 2:] == 0) and np.all(L[:, :2] > 0)
+    assert np.all(bad_q["page_table"].cpu().numpy()[:, 2:] == -1)
+    bound = _plan_raw([40, 30], [2, 3], 2, bt, 4, 16, 15)         # ceil(40/2) > 15
+    assert int(bound["err_flag"].item()) & mla.MLA_PLAN_ERR_BOUND
+    blk = _plan_raw([40, 30], [2, 3], 2, [[0, 9], [2, 3]], 4, 16, 20)  # id 9 >= 4
+    assert int(blk["err_flag"].item()) & mla.MLA_PLAN_ERR_BLOCKS
+    assert np.all(blk["row_lens"].cpu().numpy()[:, :2] == 0)
+    few = _plan_raw([70, 30], [2, 3], 2, bt, 4, 16, 40)           # needs 3 blocks > 2
+    assert int(few["err_flag"].item()) & mla.MLA_PLAN_ERR_BLOCKS
+    rows = _plan_raw([40, 30], [2, 3], 2, bt, 4, 16, 20, R=4)     # q_start[N] != R
+    assert int(rows["err_flag"].item()) & mla.MLA_PLAN_ERR_ROWS
+
+
+def test_zero_query_pins_every_window():
+    """q = 0: every score is 0, so the final lse is ln(window) and each shard's
+    lse is ln(its row length) -- one token too many or too few on any shard
+    moves the lse by about 1/L, far beyond 1e-3 at these lengths."""
+    spec = small_spec(N=6, W=4, qlen=5, seq_range=(5, 120), block_size=16, H=2)
+    inp = wl.make_workload(spec, seed=4, q_mode="zero")
+    got = run_gpu(inp, nseg=2, want_shards=True)
+    ref = _check_plan(inp, got)
+    for i in range(inp["N"]):
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        for t in range(Q):
+            w = inp["seq_lens"][i] - Q + 1 + t
+            assert np.allclose(got["lse"][qs + t], math.log(w), atol=1e-4)
+            for r in range(4):
+                L = ref["row_lens"][r, qs + t]
+                want = math.log(L) if L else -math.inf
+                assert max_err(got["shard_lse"][r, qs + t], np.full(2, want)) <= 1e-4
+
+
+def test_output_discriminates_off_by_one_window():
+    """The GPU output is closer to the oracle with the pages' window than to
+    the oracle with the window one position longer (the garbled snippet
+    reading), on every row where those two oracles differ clearly."""
+    spec = small_spec(N=6, W=2, qlen=4, seq_range=(10, 40), block_size=16, H=4)
+    inp = wl.make_workload(spec, seed=2)
+    got = run_gpu(inp)
+    q = orc.decode_bf16(inp["q_bits"])
+    checked = 0
+    for i in range(inp["N"]):
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        S = int(inp["seq_lens"][i])
+        K = orc.gather_request_kv(inp["kv_bits"], "bf16", 1.0, inp["block_table"][i], S, 2, 16)
+        good, _ = orc.attention_rows(q[qs:qs + Q], K, S, Q, inp["sm_scale"])
+        for t in range(Q - 1):  # rows whose window can grow by one inside S
+            w_bad = S - Q + 2 + t       # one position more than the pages' window
+            bad, _ = orc.attention_rows(q[qs + t:qs + t + 1], K, w_bad, 1, inp["sm_scale"])
+            if np.abs(good[t] - bad[0]).max() < 4 * TOL_OUT["bf16"]:
+                continue
+            checked += 1
+            dg = np.abs(got["out"][qs + t] - good[t]).max()
+            db = np.abs(got["out"][qs + t] - bad[0]).max()
+            assert dg < db and dg <= TOL_OUT["bf16"]
+    assert checked >= 6
+
+
+def test_fp8_every_finite_code_decodes():
+    """Fill every used cache slot with codes cycling through all 254 finite
+    e4m3fn values; the oracle decodes them from the bit definition."""
+    spec = small_spec(N=2, W=2, kv_dtype="fp8_e4m3", qlen=3, H=4, seq_range=(200, 300))
+    inp = wl.make_workload(spec, seed=6)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    cache = inp["kv_bits"]
+    used = cache != wl.E4M3_NAN
+    cache[used] = np.resize(finite, int(used.sum()))
+    inp["kv_scale"] = 1.0 / 448.0
+    got = run_gpu(inp)
+    out_ref, lse_ref = orc.verify_reference(inp)
+    assert out_excess(got["out"], out_ref, "fp8_e4m3") <= 1.0
+    assert max_err(got["lse"], lse_ref) <= TOL_LSE
+
+
+def test_side_stream_matches_default_stream():
+    inp = wl.make_workload(small_spec(), seed=8)
+    a = run_gpu(inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_gpu(inp, stream=s)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+
+
+# -------------------------------------------------------- named workloads ---
+
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
+def test_named_workload_parity(name):
+    """The five workloads at full size: plan bit-exact; out / lse against the
+    oracle on sampled requests (the longest and shortest included); every
+    output finite (cache slots outside any window hold NaN canaries)."""
+    inp = named_workload(name)
+    say(f"workload {name}: R={inp['R']} sum S={int(inp['seq_lens'].sum())}")
+    got = run_gpu(inp)
+    _check_plan(inp, got)
+    assert np.all(np.isfinite(got["out"])) and np.all(np.isfinite(got["lse"]))
+    k = {"tiny_decode": 2, "verify_dcp8": 32, "fp8_verify_dcp4": 8,
+         "long_context_dcp8": 3, "ragged_mixed": 6}[name]
+    reqs = sample_requests(inp, k)
+    eo, el, ex, *_ = compare_requests(inp, got, reqs)
+    say(f"workload {name}: requests {reqs} max|dout|={eo:.3e} max|dlse|={el:.3e} "
+        f"excess={ex:.3f}")
+    assert ex <= 1.0
+    assert el <= TOL_LSE

@@ -180,3 +180,21 @@ def algorithmic_flops(inp) -> int:
     Q = inp["qlens"].astype(np.int64)
     window_sum = Q * (S - Q) + Q * (Q + 1) // 2
     return int(window_sum.sum()) * int(inp["H"]) * (2 * 576 + 2 * 512)
+
+
+def to_device(inp, device="cuda"):
+    """Move a workload's inputs to the GPU in the layouts the library takes."""
+    import torch as _t
+    q = _t.from_numpy(inp["q_bits"].view(np.int16)).view(_t.bfloat16).to(device)
+    if inp["kv_dtype"] == "bf16":
+        kv = _t.from_numpy(inp["kv_bits"].view(np.int16)).view(_t.bfloat16).to(device)
+    else:
+        kv = _t.from_numpy(inp["kv_bits"]).to(device)
+    i32 = lambda a: _t.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    return {
+        "q": q, "kv": kv, "seq_lens": i32(inp["seq_lens"]), "q_start": i32(inp["q_start"]),
+        "block_table": i32(inp["block_table"]), "num_blocks": int(inp["num_blocks"]),
+        "block_size": int(inp["block_size"]), "R": int(inp["R"]), "W": int(inp["W"]),
+        "max_kv_seq_len": int(inp["max_kv_seq_len"]), "max_qlen": int(np.max(inp["qlens"])),
+        "sm_scale": float(inp["sm_scale"]), "kv_scale": float(inp["kv_scale"]),
+    }

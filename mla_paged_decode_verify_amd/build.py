@@ -25,7 +25,12 @@ SOURCES = ["api.cpp", "plan.hip", "attn.hip", "merge.hip"]
 
 # Packed fp32 instructions are switched off: hipcc -O3 would otherwise form
 # them from plain float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs: the attention kernel rescales its
+                # output accumulators with plain VALU multiplies, and this keeps
+                # them out of AGPRs (whose copies would cost 256 moves a tile);
+                # the query fragments go to AGPRs instead.
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 

@@ -21,16 +21,16 @@ LIB_NAME = "libmla_verify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.hip", "attn.hip", "merge.hip"]
+SOURCES = ["api.cpp", "plan.hip", "attn_bf16.hip", "attn_fp8.hip", "merge.hip"]
 
 # Packed fp32 instructions are switched off: hipcc -O3 would otherwise form
 # them from plain float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # MFMA accumulators in VGPRs: the attention kernel rescales its
-                # output accumulators with plain VALU multiplies, and this keeps
-                # them out of AGPRs (whose copies would cost 256 moves a tile);
-                # the query fragments go to AGPRs instead.
-                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extras. The attention kernels keep their 128-register output
+# accumulators in VGPRs (they rescale them with plain VALU multiplies; AGPR
+# copies would cost 256 moves a tile) and the query fragments in AGPRs.
+_ATTN = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"attn_bf16.hip": _ATTN, "attn_fp8.hip": _ATTN}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
@@ -62,7 +62,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *COMMON_FLAGS, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []),
+               "-c", os.path.join(CSRC, src), "-o", obj]
         if resource_usage and src.endswith(".hip"):
             cmd += ["-Rpass-analysis=kernel-resource-usage"]
         _run(cmd, verbose or resource_usage)

@@ -1,0 +1,124 @@
+// Split-K segmented MLA attention partials, bf16 KV cache.
+//
+// The quantities computed, the work decomposition and the per-tile
+// computation are those of attn_common.h. Specific to this kernel:
+//  * Tiles go straight from HBM to LDS (global_load_lds_dwordx4: one 1 KB
+//    instruction per token's latent part, one per 8 tokens' rope parts), so no
+//    registers hold data in flight. While tile k is computed, tile k+1 streams
+//    in, one instruction per QK K-step; two LDS buffers alternate.
+//  * Page-table entries: when sub-pages hold 16+ tokens, a wave's 16-token
+//    slice of a tile lies in one sub-page, so one vector load gives a wave the
+//    entries of 64 tiles (one per lane), read out with v_readlane; no load of
+//    a page entry sits between two tiles. Smaller sub-pages take per-token
+//    entries, fetched at the start of each tile.
+#include "attn_common.h"
+
+namespace mla {
+namespace {
+
+// Slice pages of 64 consecutive tiles for one wave: lane j holds the sub-page
+// of tokens tb0 + 64 j + 16 w .. +15 (the last in-range entry past the
+// segment end; tokens there are masked and read from the zero row).
+__device__ __forceinline__ int32_t slice_pages(const AttnArgs& a, const int32_t* pt_row, int tb0,
+                                               int hi, int wave, int lane) {
+  const int64_t tok = min((int64_t)tb0 + (int64_t)kTile * lane + 16 * wave, (int64_t)hi - 1);
+  return pt_row[tok >> a.page_shift];
+}
+
+template <bool SLICE>
+__global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
+  // Two separate arrays (not one indexed one), so that the compiler can tell
+  // the buffer being read from the buffer the direct loads are filling.
+  __shared__ __align__(16) unsigned char buf0[kBufBytes];
+  __shared__ __align__(16) unsigned char buf1[kBufBytes];
+  __shared__ PExchange px;
+  __shared__ RowExchange rx;
+  const WorkUnit u = decode_unit(a, blockIdx.x);
+  if (!u.valid) return;
+  const int lo = u.lo, hi = u.hi;
+  if (lo >= hi) return;                     // segment inactive for the whole group
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 1;                  // row group: 32 rows
+  const int c = wave & 1;                   // token half (QK) / latent half (PV)
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kTokBytesBf16;
+  const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
+
+  // ---- first tile in flight before anything else
+  int32_t vpg = 0;                          // SLICE: pages of tiles 64q .. 64q + 63
+  Bf16Pages pg;
+  if constexpr (SLICE) {
+    vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
+    const int32_t sp0 = __builtin_amdgcn_readlane(vpg, 0);
+#pragma unroll
+    for (int j = 0; j < 18; ++j) issue_one_slice(a, pool, sp0, lo, hi, buf0, wave, lane, j);
+  } else {
+    pg.fetch(a, pt_row, lo, hi, wave, lane);
+    issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane);
+  }
+
+  int mrow[2], hi_row[2];
+  bool row_ok[2];
+  lane_rows(a, u, g, r16, mrow, hi_row, row_ok);
+  bf16x8 qf[2][kQSteps];
+  load_q(a, u, mrow, row_ok, g4, qf);
+
+  WaveState st;
+  state_init(st);
+
+  // One tile (index kt from the segment start): wait until `cur` holds it,
+  // start filling `nxt` with the next tile, compute on `cur`.
+  auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
+    const bool more = tb + kTile < hi;
+    MLA_WAIT_VMCNT(0);                      // this wave's loads of `cur` have landed ...
+    lds_barrier();                          // ... for every wave; `nxt` is no longer read
+    int32_t sp = 0;
+    if constexpr (SLICE) {
+      if (more) {
+        const int nk = kt + 1;
+        if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
+        sp = __builtin_amdgcn_readlane(vpg, nk & 63);
+      }
+    } else {
+      if (more) {
+        pg.fetch(a, pt_row, tb + kTile, hi, wave, lane);
+        issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane);
+      }
+    }
+    auto issue = [&](int j) {
+      if constexpr (SLICE) {
+        if (more) issue_one_slice(a, pool, sp, tb + kTile, hi, nxt, wave, lane, j);
+      }
+    };
+    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
+  };
+  int kt = 0;
+  for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
+    step(buf0, buf1, tb, kt);
+    if (tb + kTile >= hi) break;
+    step(buf1, buf0, tb + kTile, kt + 1);
+  }
+
+  store_partials(a, u, st, rx, mrow, row_ok, g, c, lane);
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s) {
+  const int64_t blocks = (int64_t)a.N * a.W * a.nseg * a.mblocks;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (fp8) return launch_attn_fp8(a, blocks, s);
+  if (a.page_size >= 16)
+    attn_bf16_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  else
+    attn_bf16_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,481 @@
+// Shared pieces of the attention kernels (gfx950, wave64): LDS tile layout,
+// sources of KV tokens in the paged pool, the direct HBM -> LDS loads of bf16
+// tiles, work-unit decoding and the Q fragments.
+//
+// What the kernels compute (vLLM PR #51705 digest, Implementation breakdown
+// items 2-4 and the merge snippet): for every shard r, verify row rho, head h
+// and split-K segment s, over the segment's local tokens that the row may see,
+//   m2 = max(score * log2 e), e = sum 2^(score*log2e - m2),
+//   O  = sum 2^(score*log2e - m2) * v,   score = sm_scale * <q, k> (576 dims),
+// with v the 512 latent dims of the same cache entry (SGLang PR #34432 report,
+// _forward_verify_dcp snippet). The partition follows the pages'
+// tiles_per_segment = ceil(len / (segments * tile)) with len the group's
+// longest row and tile = the sub-page size.
+//
+// One workgroup = 4 waves = one work unit (request i, shard r, segment s,
+// 64-row block of the request's Q_i*H (row, head) pairs). All rows of a
+// request share the shard's KV, so a KV tile is read from HBM once per block.
+// LDS tile layout (64 tokens): latent [64][512 bf16 + 16 pad] -- with this row
+// stride neither the K-fragment reads nor the transposed V reads hit bank
+// conflicts (measured with SQ_LDS_BANK_CONFLICT) -- and rope [64][8 chunks of
+// 16 B] with chunk c of token t in slot c ^ (t & 7).
+#pragma once
+
+#include "internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kTile = 64;                  // tokens per KV tile
+constexpr int kLatRow = 1056;              // 512 bf16 latent + 32 B pad (no bank conflicts)
+constexpr int kLatBytes = kTile * kLatRow;
+constexpr int kRopeRow = 128;              // 64 bf16 rope = 8 chunks of 16 B
+constexpr int kRopeBytes = kTile * kRopeRow;
+constexpr int kBufBytes = kLatBytes + kRopeBytes;
+constexpr int kThreads = 256;
+constexpr int kQSteps = kHeadDim / 32;     // 18 MFMA K-steps (32 dims) for QK^T
+constexpr int kLatQSteps = kVDim / 32;     // the first 16 read the latent region
+constexpr int kNTiles = kVDim / 16;        // 32 output tiles of 16 latent dims
+constexpr int kTokBytesBf16 = kHeadDim * 2;
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.f;       // log2 units
+
+// Slot permutation of the 16-byte chunks of latent row r.
+__device__ __forceinline__ int lat_swz(int r) { return 0; }
+// Byte offset of 16-byte chunk c (dims 8c..8c+7) of latent row r in a tile.
+__device__ __forceinline__ int lat_off(int r, int c) { return r * kLatRow + ((c ^ lat_swz(r)) << 4); }
+
+// Source of tokens outside the segment: a row of zeros, so that masked
+// positions hold finite values (0 * NaN would poison the PV product).
+__device__ __align__(16) unsigned char g_zero_token[kTokBytesBf16];
+
+// max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane groups of a
+// wave), with the gfx950 lane-swap instructions instead of an LDS round trip.
+__device__ __forceinline__ float max4(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum4(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Address of token `tok` with sub-page id `sp`, or the zero row when the token
+// is past the segment end `hi` or sp is outside the pool.
+template <int TOKB>
+__device__ inline const unsigned char* token_src(const AttnArgs& a, const unsigned char* pool,
+                                                 int32_t sp, int tok, int hi) {
+  if (tok >= hi || sp < 0 || sp >= a.num_subpages) return g_zero_token;
+  const int64_t t = ((int64_t)sp << a.page_shift) + (tok & (a.page_size - 1));
+  return pool + t * TOKB;
+}
+
+// Page-table entries one wave needs to issue a bf16 tile: lane l holds the
+// entry of latent token 16w + (l & 15) and of rope tokens 16w + (l >> 3) and
+// 16w + 8 + (l >> 3).
+// The loads are unconditional (clamped index; the consumer checks tok < hi),
+// so that every fetch issues exactly three vector memory instructions and
+// nothing waits for them until they are used.
+__device__ inline int32_t subpage_always(const AttnArgs& a, const int32_t* pt_row, int tok,
+                                         int hi) {
+  return pt_row[min(tok, hi - 1) >> a.page_shift];
+}
+struct Bf16Pages {
+  int32_t lat, rope0, rope1;
+  __device__ inline void fetch(const AttnArgs& a, const int32_t* pt_row, int tb, int hi,
+                               int wave, int lane) {
+    lat = subpage_always(a, pt_row, tb + 16 * wave + (lane & 15), hi);
+    rope0 = subpage_always(a, pt_row, tb + 16 * wave + (lane >> 3), hi);
+    rope1 = subpage_always(a, pt_row, tb + 16 * wave + 8 + (lane >> 3), hi);
+  }
+};
+
+// Workgroup barrier that orders LDS traffic only. __syncthreads() would also
+// wait for every outstanding global load, i.e. for the prefetches this
+// kernel deliberately keeps in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt with vmcnt = n and no wait on the other counters (gfx9 encoding).
+#define MLA_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 0x3) << 14))
+
+// One direct HBM -> LDS load: each lane's 16 bytes at `src` land at
+// lds + 16 * lane. Written as inline assembly so that the compiler does not
+// track the LDS write: it cannot tell that the loads in flight target the
+// other tile buffer, and would otherwise wait for them before LDS accesses
+// it cannot prove disjoint. The kernels order these loads themselves
+// (s_waitcnt vmcnt + barrier before a buffer is read or refilled). M0 holds
+// the LDS base; one wait state separates its write from the load.
+__device__ __forceinline__ void dma16(const void* src, const unsigned char* lds) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const lds_void*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "m0");
+}
+
+// bf16: direct HBM -> LDS load number j (0..17) of this wave for tile
+// [tb, tb + 64) into `dst`: j < 16 is the latent part of token 16w + j (one
+// 1 KB instruction), j = 16, 17 the rope parts of tokens 16w + 8(j-16) + 0..7.
+__device__ __forceinline__ void issue_one_bf16(const AttnArgs& a, const unsigned char* pool,
+                                               const Bf16Pages& pg, int tb, int hi,
+                                               unsigned char* dst, int wave, int lane, int j) {
+  if (j < 16) {
+    const int row = 16 * wave + j;
+    const int32_t sp = __builtin_amdgcn_readlane(pg.lat, j);
+    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi);
+    // slot `lane` of the row holds chunk lane ^ swz(row)
+    dma16(src + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
+  } else {
+    const int jj = j - 16;
+    const int u = lane >> 3;                // token within the 8-token group
+    const int chunk = (lane & 7) ^ u;       // slot (lane & 7) holds chunk ^ u
+    const int row = 16 * wave + 8 * jj + u;
+    const unsigned char* src =
+        token_src<kTokBytesBf16>(a, pool, jj ? pg.rope1 : pg.rope0, tb + row, hi);
+    dma16(src + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
+  }
+}
+
+// All 18 loads of this wave for one tile.
+__device__ inline void issue_tile_bf16(const AttnArgs& a, const unsigned char* pool,
+                                       const Bf16Pages& pg, int tb, int hi, unsigned char* dst,
+                                       int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 18; ++j) issue_one_bf16(a, pool, pg, tb, hi, dst, wave, lane, j);
+}
+
+// Slice-page variants of the bf16 loads (all 16 tokens of the slice in `sp`).
+__device__ __forceinline__ void issue_one_slice(const AttnArgs& a, const unsigned char* pool,
+                                                int32_t sp, int tb, int hi, unsigned char* dst,
+                                                int wave, int lane, int j) {
+  if (j < 16) {
+    const int row = 16 * wave + j;
+    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi);
+    dma16(src + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
+  } else {
+    const int jj = j - 16;
+    const int u = lane >> 3;
+    const int chunk = (lane & 7) ^ u;
+    const int row = 16 * wave + 8 * jj + u;
+    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi);
+    dma16(src + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
+  }
+}
+
+// Work unit of a workgroup and the segment [lo, hi) of local tokens it covers
+// (valid: the request's rows are well formed and the row block exists).
+struct WorkUnit {
+  int i, r, s, mb;
+  int qs, Q, M, m0, last;
+  int lo, hi;
+  bool valid;
+};
+__device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
+  WorkUnit u;
+  u.mb = b % a.mblocks;
+  b /= a.mblocks;
+  u.s = b % a.nseg;
+  b /= a.nseg;
+  u.r = b % a.W;
+  u.i = b / a.W;
+  u.qs = a.q_start[u.i];
+  u.Q = a.q_start[u.i + 1] - u.qs;
+  u.M = u.Q * a.H;                          // (row, head) pairs of the request
+  u.m0 = u.mb * kAttnRows;
+  u.valid = !(u.qs < 0 || u.Q <= 0 || u.qs + u.Q > a.R || u.m0 >= u.M);
+  u.last = u.qs + u.Q - 1;                  // the group's longest row
+  u.lo = u.hi = 0;
+  if (!u.valid) return u;
+  int Lg = a.row_lens[(int64_t)u.r * a.R + u.last];
+  Lg = min(Lg, a.pt_width * a.page_size);
+  const int span = (Lg + a.nseg * a.page_size - 1) / (a.nseg * a.page_size) * a.page_size;
+  u.lo = u.s * span;
+  u.hi = min(u.lo + span, Lg);             // lo >= hi: segment inactive for the group
+  return u;
+}
+
+// This lane's two rows (rows 32g + 16rt + l%16 of the block) and the part of
+// the segment each may see.
+__device__ inline void lane_rows(const AttnArgs& a, const WorkUnit& u, int g, int r16,
+                                 int (&mrow)[2], int (&hi_row)[2], bool (&row_ok)[2]) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    mrow[rt] = u.m0 + 32 * g + 16 * rt + r16;
+    row_ok[rt] = mrow[rt] < u.M;
+    const int Lrow = row_ok[rt] ? a.row_lens[(int64_t)u.r * a.R + u.qs + mrow[rt] / a.H] : 0;
+    hi_row[rt] = min(u.hi, Lrow);
+  }
+}
+
+// Q fragments (B operand of S^T = K Q^T): 8 dims per lane per K-step.
+__device__ inline void load_q(const AttnArgs& a, const WorkUnit& u, const int (&mrow)[2],
+                              const bool (&row_ok)[2], int g4, bf16x8 (&qf)[2][kQSteps]) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const uint16_t* qp =
+        a.q + ((int64_t)u.qs * a.H + (row_ok[rt] ? mrow[rt] : 0)) * kHeadDim + 8 * g4;
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
+      uint4 v = row_ok[rt] ? *reinterpret_cast<const uint4*>(qp + 32 * k) : make_uint4(0, 0, 0, 0);
+      qf[rt][k] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+}
+
+// K fragment (A operand of S^T = K Q^T) for K-step k: token `tok` of the tile,
+// 8 dims 32k + 8(l/16) .. +7 of lane l.
+__device__ __forceinline__ bf16x8 k_fragment(const unsigned char* tile, int tok, int k, int g4) {
+  if (k < kLatQSteps)
+    return *reinterpret_cast<const bf16x8*>(tile + lat_off(tok, 4 * k + g4));
+  const int chunk = 4 * (k - kLatQSteps) + g4;
+  return *reinterpret_cast<const bf16x8*>(tile + kLatBytes + tok * kRopeRow +
+                                          16 * (chunk ^ (tok & 7)));
+}
+
+// ---------------------------------------------------------------------------
+// Per-tile computation, shared by the bf16 and fp8 kernels.
+//
+// Wave (g, c) of a workgroup: rows 32g..32g+31 of the block. For every 64-token
+// tile it computes S^T for tokens 32c..32c+31 of the tile, and O^T for latent
+// dims 256c..256c+255 over all 64 tokens, so the two waves of a row group trade
+// their row maxima and their P fragments through LDS once per tile each.
+//
+// S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with Q in
+// registers. The S^T accumulator layout is already the B-operand layout of the
+// PV product (under a fixed token permutation inside each 32-token K-step), so
+// P never moves between the lanes of a wave; V^T fragments come straight from
+// the row-major tile with ds_read_b64_tr_b16 in the same permutation.
+//
+// Online softmax in base 2 with a lazily refreshed reference: O and the sum
+// are rescaled only when the row maximum passes the reference by more than 8
+// (P <= 256, harmless for bf16 P and fp32 sums); at the end they are rescaled
+// once to the true maximum, which is what is stored. Both waves of a row
+// group see the same tile maxima and so make the same decisions.
+
+// Accumulation state of one wave: 32 rows (two 16-row tiles) x 256 latent dims.
+struct WaveState {
+  f32x4 o[2][kNTiles / 2];  // O^T tiles: lane l holds dims 256c + 16n + 4(l/16) + 0..3
+  float m_ref[2];           // reference exponent of o and l_part (row-uniform)
+  float m_true[2];          // true running maximum (row-uniform)
+  float l_part[2];          // this lane's share of the exp2 sum over this wave's tokens
+};
+
+// Row maxima and P fragments handed to the partner wave, once per tile each.
+struct PExchange {
+  uint4 p[2][2][2][64];     // [g][c][row tile][lane]: bf16 P of wave (g, c)'s tokens
+  float mx[2][2][2][16];    // [g][c][row tile][row]: its maxima over its tokens
+};
+
+// End-of-segment exchange of row sums between partner waves.
+struct RowExchange {
+  float l[2][2][2][16];     // [g][c][row tile][row]
+};
+
+__device__ __forceinline__ void state_init(WaveState& st) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int n = 0; n < kNTiles / 2; ++n) st.o[rt][n] = f32x4{};
+    st.m_ref[rt] = kNegInf;
+    st.m_true[rt] = kNegInf;
+    st.l_part[rt] = 0.f;
+  }
+}
+
+// Scores, softmax and PV for one 64-token tile held in `tile` (LDS).
+// `issue(k)` is called once per QK K-step (k = 0..17), so that the loads of
+// the next tile can be spread over the MFMA work.
+template <class Issue>
+__device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ tile,
+                                             PExchange* __restrict__ px,
+                                             const bf16x8 (&qf)[2][kQSteps],
+                                             WaveState& st, int tb, const int (&hi_row)[2],
+                                             float qk_scale_log2, int g, int c, int lane,
+                                             Issue&& issue) {
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  // ---- S^T[32 tokens x 32 rows]: per K-step two K fragments (16 tokens each),
+  // each feeding both row tiles. Fragments are read two K-steps ahead of their
+  // MFMAs (a 3-slot ring); the scheduling barriers keep that order.
+  f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};  // [row tile][token tile]
+  bf16x8 kr[3][2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    kr[k][0] = k_fragment(tile, 32 * c + r16, k, g4);
+    kr[k][1] = k_fragment(tile, 32 * c + 16 + r16, k, g4);
+  }
+#pragma unroll
+  for (int k = 0; k < kQSteps; ++k) {
+    if (k + 2 < kQSteps) {
+      kr[(k + 2) % 3][0] = k_fragment(tile, 32 * c + r16, k + 2, g4);
+      kr[(k + 2) % 3][1] = k_fragment(tile, 32 * c + 16 + r16, k + 2, g4);
+    }
+    issue(k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k % 3][tt], qf[rt][k],
+                                                               sacc[rt][tt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- scale, mask, row maximum over this wave's 32 tokens. Element e of a
+  // row tile is token 32c + 16(e/4) + 4(l/16) + e%4.
+  float mx[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    mx[rt] = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = tb + 32 * c + 16 * tt + 4 * g4 + v;
+        const float x = tok < hi_row[rt] ? sacc[rt][tt][v] * qk_scale_log2 : kNegInf;
+        sacc[rt][tt][v] = x;
+        mx[rt] = fmaxf(mx[rt], x);
+      }
+    }
+    mx[rt] = max4(mx[rt]);
+    if (g4 == 0) px->mx[g][c][rt][r16] = mx[rt];
+  }
+
+  // ---- V^T reads for the first PV steps go out before the barrier. Lane i of
+  // each 16-lane group points at dims 16n + 4(i%4) of token t0 + i/4; the
+  // transposed read hands it dim 16n + i of tokens t0..t0+3. Steps
+  // t = 16kk + n (K-step kk, 16-dim tile n); each step's two reads are issued
+  // three steps ahead of its MFMAs (a 4-slot ring).
+  const int i16 = lane & 15;
+  auto vread = [&](int t, i16x4& lo4, i16x4& hi4) {
+    const int kk = t >> 4, n = t & 15;
+    const int row = 32 * kk + 4 * g4 + (i16 >> 2);
+    const int ch = 32 * c + 2 * n + ((i16 & 3) >> 1);
+    const int byte = 8 * (i16 & 1);
+    lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + lat_off(row, ch) + byte));
+    hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(tile + lat_off(row + 16, ch) + byte));
+  };
+  constexpr int kPvSteps = 2 * (kNTiles / 2);
+  i16x4 vr[4][2];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) vread(t, vr[t][0], vr[t][1]);
+
+  lds_barrier();
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    // the partner saw the other 32 tokens; both waves now hold the same tile max
+    mx[rt] = fmaxf(mx[rt], px->mx[g][c ^ 1][rt][r16]);
+    st.m_true[rt] = fmaxf(st.m_true[rt], mx[rt]);
+  }
+
+  // ---- lazily refreshed reference (identical decisions on both waves)
+  const bool refresh0 = mx[0] > st.m_ref[0] + kRescaleSlack;
+  const bool refresh1 = mx[1] > st.m_ref[1] + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(refresh0 || refresh1) != 0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const bool rf = rt ? refresh1 : refresh0;
+      const float alpha = rf ? __builtin_amdgcn_exp2f(st.m_ref[rt] - mx[rt]) : 1.f;
+      st.l_part[rt] *= alpha;
+#pragma unroll
+      for (int n = 0; n < kNTiles / 2; ++n) st.o[rt][n] *= alpha;
+      st.m_ref[rt] = rf ? mx[rt] : st.m_ref[rt];
+    }
+  }
+
+  // ---- P of this wave's tokens; publish it for the partner
+  bf16x8 pown[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const float m_use = st.m_ref[rt] == kNegInf ? 0.f : st.m_ref[rt];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = sacc[rt][e >> 2][e & 3];
+      const float p = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x - m_use);
+      st.l_part[rt] += p;
+      pown[rt][e] = (__bf16)p;
+    }
+    px->p[g][c][rt][lane] = __builtin_bit_cast(uint4, pown[rt]);
+  }
+  lds_barrier();
+  // K-step kk of the PV product covers tokens 32kk..32kk+31, i.e. half kk
+  bf16x8 pf[2][2];  // [token half][row tile]
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const bf16x8 ppart = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][rt][lane]);
+    pf[0][rt] = c == 0 ? pown[rt] : ppart;
+    pf[1][rt] = c == 0 ? ppart : pown[rt];
+  }
+
+  // ---- O^T[256 dims x 32 rows] += V^T[256 x 64 tokens] P^T[64 x 32]
+#pragma unroll
+  for (int t = 0; t < kPvSteps; ++t) {
+    if (t + 3 < kPvSteps) vread(t + 3, vr[(t + 3) % 4][0], vr[(t + 3) % 4][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kk = t >> 4, n = t & 15;
+    const bf16x8 va = __builtin_bit_cast(
+        bf16x8, __builtin_shufflevector(vr[t % 4][0], vr[t % 4][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[kk][rt], st.o[rt][n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// End of the segment: add the partner wave's row sums and write the partials
+// (maximum, sum and O relative to the maximum).
+__device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit& u,
+                                               const WaveState& st, RowExchange& rx,
+                                               const int (&mrow)[2], const bool (&row_ok)[2],
+                                               int g, int c, int lane) {
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  float l_row[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    l_row[rt] = sum4(st.l_part[rt]);
+    if (g4 == 0) rx.l[g][c][rt][r16] = l_row[rt];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    if (!row_ok[rt]) continue;
+    const float L = l_row[rt] + rx.l[g][c ^ 1][rt][r16];
+    // move O and l from the reference exponent to the true maximum
+    float fix = 1.f;
+    if (st.m_true[rt] != kNegInf) fix = __builtin_amdgcn_exp2f(st.m_ref[rt] - st.m_true[rt]);
+    const float vs = fix * a.v_scale;
+    const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow[rt]) * a.nseg + u.s;
+    if (c == 0 && g4 == 0) {
+      a.segm_max[e] = st.m_true[rt];
+      a.segm_expsum[e] = L * fix;
+    }
+    float* op = a.segm_out + e * kVDim + 256 * c + 4 * g4;
+#pragma unroll
+    for (int n = 0; n < kNTiles / 2; ++n) {
+      *reinterpret_cast<float4*>(op + 16 * n) =
+          make_float4(st.o[rt][n][0] * vs, st.o[rt][n][1] * vs, st.o[rt][n][2] * vs,
+                      st.o[rt][n][3] * vs);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace mla

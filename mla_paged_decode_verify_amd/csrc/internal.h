@@ -60,6 +60,7 @@ struct MergeArgs {
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 // Rows of one attention workgroup (two groups of 32 rows).

@@ -110,7 +110,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.N * a.W * a.nseg * a.mblocks;
+  const int64_t units = (int64_t)a.N * a.W * a.nseg;
+  const int64_t blocks = (units + 7) / 8 * 8 * a.mblocks;   // see decode_unit
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (fp8) return launch_attn_fp8(a, blocks, s);

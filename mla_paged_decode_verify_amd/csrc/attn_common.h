@@ -184,14 +184,22 @@ struct WorkUnit {
   int lo, hi;
   bool valid;
 };
+// Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8): the row
+// blocks of one (request, shard, segment) unit are given ids that land on the
+// same XCD one after another, so that they run side by side and share that
+// XCD's L2 copy of the unit's KV. The grid covers ceil(units / 8) * 8 units.
 __device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
   WorkUnit u;
-  u.mb = b % a.mblocks;
-  b /= a.mblocks;
-  u.s = b % a.nseg;
-  b /= a.nseg;
-  u.r = b % a.W;
-  u.i = b / a.W;
+  const int slot = b >> 3;
+  u.mb = slot % a.mblocks;
+  int unit = (slot / a.mblocks) * 8 + (b & 7);
+  u.valid = unit < a.N * a.W * a.nseg;
+  u.lo = u.hi = 0;
+  if (!u.valid) return u;
+  u.s = unit % a.nseg;
+  unit /= a.nseg;
+  u.r = unit % a.W;
+  u.i = unit / a.W;
   u.qs = a.q_start[u.i];
   u.Q = a.q_start[u.i + 1] - u.qs;
   u.M = u.Q * a.H;                          // (row, head) pairs of the request

@@ -5,7 +5,8 @@
 //  * Tiles go straight from HBM to LDS (global_load_lds_dwordx4: one 1 KB
 //    instruction per token's latent part, one per 8 tokens' rope parts), so no
 //    registers hold data in flight. While tile k is computed, tile k+1 streams
-//    in, one instruction per QK K-step; two LDS buffers alternate.
+//    in, issued two instructions per QK K-step over the first half of the QK
+//    work; two LDS buffers alternate.
 //  * Page-table entries: when sub-pages hold 16+ tokens, a wave's 16-token
 //    slice of a tile lies in one sub-page, so one vector load gives a wave the
 //    entries of 64 tiles (one per lane), read out with v_readlane; no load of
@@ -90,9 +91,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
         issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane);
       }
     }
+    // two loads per QK K-step over the first nine K-steps: the next tile's
+    // data goes out early, without one long stall on issue
     auto issue = [&](int j) {
       if constexpr (SLICE) {
-        if (more) issue_one_slice(a, pool, sp, tb + kTile, hi, nxt, wave, lane, j);
+        if (more && j < 9) {
+          issue_one_slice(a, pool, sp, tb + kTile, hi, nxt, wave, lane, 2 * j);
+          issue_one_slice(a, pool, sp, tb + kTile, hi, nxt, wave, lane, 2 * j + 1);
+        }
       }
     };
     compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);

@@ -48,6 +48,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   const int g4 = lane >> 4;
 
   const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kTokBytesBf16;
+  const unsigned char* zero = zero_row();
   const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
 
   // ---- first tile in flight before anything else
@@ -55,22 +56,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   Bf16Pages pg;
   if constexpr (SLICE) {
     vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
-    const int32_t sp0 = __builtin_amdgcn_readlane(vpg, 0);
+    const SliceSrc v0 = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, 0), lo + 16 * wave, hi);
 #pragma unroll
-    for (int j = 0; j < 18; ++j) issue_one_slice(a, pool, sp0, lo, hi, buf0, wave, lane, j);
+    for (int j = 0; j < 18; ++j) issue_slice(v0, zero, buf0, wave, lane, j);
   } else {
     pg.fetch(a, pt_row, lo, hi, wave, lane);
-    issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane);
+    issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane, zero);
   }
 
+  // ---- Q through the second tile buffer (free until the first tile's loads
+  // of the next tile, which come after the first step's barrier)
+  issue_q_tile(a, u, buf1, wave, lane, zero);
   int mrow[2], hi_row[2];
   bool row_ok[2];
   lane_rows(a, u, g, r16, mrow, hi_row, row_ok);
-  bf16x8 qf[2][kQSteps];
-  load_q(a, u, mrow, row_ok, g4, qf);
-
   WaveState st;
   state_init(st);
+  MLA_WAIT_VMCNT(0);
+  lds_barrier();
+  bf16x8 qf[2][kQSteps];
+  read_q(buf1, g, lane, qf);
 
   // One tile (index kt from the segment start): wait until `cur` holds it,
   // start filling `nxt` with the next tile, compute on `cur`.
@@ -78,17 +83,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
     const bool more = tb + kTile < hi;
     MLA_WAIT_VMCNT(0);                      // this wave's loads of `cur` have landed ...
     lds_barrier();                          // ... for every wave; `nxt` is no longer read
-    int32_t sp = 0;
+    SliceSrc v{zero, 0};
     if constexpr (SLICE) {
       if (more) {
         const int nk = kt + 1;
         if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
-        sp = __builtin_amdgcn_readlane(vpg, nk & 63);
+        v = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile + 16 * wave, hi);
       }
     } else {
       if (more) {
         pg.fetch(a, pt_row, tb + kTile, hi, wave, lane);
-        issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane);
+        issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane, zero);
       }
     }
     // two loads per QK K-step over the first nine K-steps: the next tile's
@@ -96,8 +101,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
     auto issue = [&](int j) {
       if constexpr (SLICE) {
         if (more && j < 9) {
-          issue_one_slice(a, pool, sp, tb + kTile, hi, nxt, wave, lane, 2 * j);
-          issue_one_slice(a, pool, sp, tb + kTile, hi, nxt, wave, lane, 2 * j + 1);
+          issue_slice(v, zero, nxt, wave, lane, 2 * j);
+          issue_slice(v, zero, nxt, wave, lane, 2 * j + 1);
         }
       }
     };
@@ -116,8 +121,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s) {
-  const int64_t units = (int64_t)a.N * a.W * a.nseg;
-  const int64_t blocks = (units + 7) / 8 * 8 * a.mblocks;   // see decode_unit
+  const int64_t blocks = (int64_t)(a.N + 7) / 8 * 8 * a.W * a.nseg * a.mblocks;  // decode_unit
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (fp8) return launch_attn_fp8(a, blocks, s);

@@ -56,6 +56,15 @@ __device__ __forceinline__ int lat_off(int r, int c) { return r * kLatRow + ((c 
 // positions hold finite values (0 * NaN would poison the PV product).
 __device__ __align__(16) unsigned char g_zero_token[kTokBytesBf16];
 
+// The zero row's address, materialised once into scalar registers (left to
+// itself the compiler re-derives it through the GOT, with a scalar load and a
+// full lgkmcnt wait, at every use).
+__device__ __forceinline__ const unsigned char* zero_row() {
+  const unsigned char* z = g_zero_token;
+  asm volatile("" : "+s"(z));
+  return z;
+}
+
 // max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane groups of a
 // wave), with the gfx950 lane-swap instructions instead of an LDS round trip.
 __device__ __forceinline__ float max4(float x) {
@@ -75,8 +84,9 @@ __device__ __forceinline__ float sum4(float x) {
 // is past the segment end `hi` or sp is outside the pool.
 template <int TOKB>
 __device__ inline const unsigned char* token_src(const AttnArgs& a, const unsigned char* pool,
-                                                 int32_t sp, int tok, int hi) {
-  if (tok >= hi || sp < 0 || sp >= a.num_subpages) return g_zero_token;
+                                                 int32_t sp, int tok, int hi,
+                                                 const unsigned char* zero) {
+  if (tok >= hi || sp < 0 || sp >= a.num_subpages) return zero;
   const int64_t t = ((int64_t)sp << a.page_shift) + (tok & (a.page_size - 1));
   return pool + t * TOKB;
 }
@@ -132,11 +142,12 @@ __device__ __forceinline__ void dma16(const void* src, const unsigned char* lds)
 // 1 KB instruction), j = 16, 17 the rope parts of tokens 16w + 8(j-16) + 0..7.
 __device__ __forceinline__ void issue_one_bf16(const AttnArgs& a, const unsigned char* pool,
                                                const Bf16Pages& pg, int tb, int hi,
-                                               unsigned char* dst, int wave, int lane, int j) {
+                                               unsigned char* dst, int wave, int lane, int j,
+                                               const unsigned char* zero) {
   if (j < 16) {
     const int row = 16 * wave + j;
     const int32_t sp = __builtin_amdgcn_readlane(pg.lat, j);
-    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi);
+    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi, zero);
     // slot `lane` of the row holds chunk lane ^ swz(row)
     dma16(src + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
   } else {
@@ -145,7 +156,7 @@ __device__ __forceinline__ void issue_one_bf16(const AttnArgs& a, const unsigned
     const int chunk = (lane & 7) ^ u;       // slot (lane & 7) holds chunk ^ u
     const int row = 16 * wave + 8 * jj + u;
     const unsigned char* src =
-        token_src<kTokBytesBf16>(a, pool, jj ? pg.rope1 : pg.rope0, tb + row, hi);
+        token_src<kTokBytesBf16>(a, pool, jj ? pg.rope1 : pg.rope0, tb + row, hi, zero);
     dma16(src + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
   }
 }
@@ -153,25 +164,41 @@ __device__ __forceinline__ void issue_one_bf16(const AttnArgs& a, const unsigned
 // All 18 loads of this wave for one tile.
 __device__ inline void issue_tile_bf16(const AttnArgs& a, const unsigned char* pool,
                                        const Bf16Pages& pg, int tb, int hi, unsigned char* dst,
-                                       int wave, int lane) {
+                                       int wave, int lane, const unsigned char* zero) {
 #pragma unroll
-  for (int j = 0; j < 18; ++j) issue_one_bf16(a, pool, pg, tb, hi, dst, wave, lane, j);
+  for (int j = 0; j < 18; ++j) issue_one_bf16(a, pool, pg, tb, hi, dst, wave, lane, j, zero);
 }
 
-// Slice-page variants of the bf16 loads (all 16 tokens of the slice in `sp`).
-__device__ __forceinline__ void issue_one_slice(const AttnArgs& a, const unsigned char* pool,
-                                                int32_t sp, int tb, int hi, unsigned char* dst,
-                                                int wave, int lane, int j) {
+// Slice-page variant of the bf16 loads: the 16 tokens t0 .. t0+15 of a wave's
+// slice of a tile lie in one sub-page `sp`, so one base address and the count
+// of tokens before the segment end describe all of them.
+struct SliceSrc {
+  const unsigned char* base;  // token t0
+  int nvalid;                 // tokens t0 .. t0 + nvalid - 1 are read; the rest are zero rows
+};
+__device__ __forceinline__ SliceSrc slice_src(const AttnArgs& a, const unsigned char* pool,
+                                              int32_t sp, int t0, int hi) {
+  SliceSrc v;
+  const bool ok = sp >= 0 && sp < a.num_subpages;
+  v.nvalid = ok ? min(max(hi - t0, 0), 16) : 0;
+  const int64_t t = ((int64_t)(ok ? sp : 0) << a.page_shift) + (t0 & (a.page_size - 1));
+  v.base = pool + t * kTokBytesBf16;
+  return v;
+}
+// Load j (0..17) of a wave's slice into `dst`: j < 16 is the latent part of
+// token 16w + j, j = 16, 17 the rope parts of tokens 16w + 8(j-16) + 0..7.
+__device__ __forceinline__ void issue_slice(const SliceSrc& v, const unsigned char* zero,
+                                            unsigned char* dst, int wave, int lane, int j) {
   if (j < 16) {
     const int row = 16 * wave + j;
-    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi);
+    const unsigned char* src = j < v.nvalid ? v.base + j * kTokBytesBf16 : zero;
     dma16(src + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
   } else {
     const int jj = j - 16;
     const int u = lane >> 3;
     const int chunk = (lane & 7) ^ u;
-    const int row = 16 * wave + 8 * jj + u;
-    const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi);
+    const int t = 8 * jj + u;                // token within the slice
+    const unsigned char* src = t < v.nvalid ? v.base + t * kTokBytesBf16 : zero;
     dma16(src + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
   }
 }
@@ -184,22 +211,23 @@ struct WorkUnit {
   int lo, hi;
   bool valid;
 };
-// Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8): the row
-// blocks of one (request, shard, segment) unit are given ids that land on the
-// same XCD one after another, so that they run side by side and share that
-// XCD's L2 copy of the unit's KV. The grid covers ceil(units / 8) * 8 units.
+// Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8). Request i
+// goes to XCD i % 8, and all its work units (every shard, segment and row
+// block) get consecutive ids on that XCD, so they run side by side: its Q,
+// and each unit's KV across row blocks, come from HBM into that XCD's L2
+// once. The grid covers ceil(N / 8) * 8 requests.
 __device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
   WorkUnit u;
   const int slot = b >> 3;
   u.mb = slot % a.mblocks;
-  int unit = (slot / a.mblocks) * 8 + (b & 7);
-  u.valid = unit < a.N * a.W * a.nseg;
+  int t = slot / a.mblocks;
+  u.s = t % a.nseg;
+  t /= a.nseg;
+  u.r = t % a.W;
+  u.i = (t / a.W) * 8 + (b & 7);
+  u.valid = u.i < a.N;
   u.lo = u.hi = 0;
   if (!u.valid) return u;
-  u.s = unit % a.nseg;
-  unit /= a.nseg;
-  u.r = unit % a.W;
-  u.i = unit / a.W;
   u.qs = a.q_start[u.i];
   u.Q = a.q_start[u.i + 1] - u.qs;
   u.M = u.Q * a.H;                          // (row, head) pairs of the request
@@ -229,18 +257,32 @@ __device__ inline void lane_rows(const AttnArgs& a, const WorkUnit& u, int g, in
   }
 }
 
-// Q fragments (B operand of S^T = K Q^T): 8 dims per lane per K-step.
-__device__ inline void load_q(const AttnArgs& a, const WorkUnit& u, const int (&mrow)[2],
-                              const bool (&row_ok)[2], int g4, bf16x8 (&qf)[2][kQSteps]) {
+// Q of the block, staged in a tile buffer: block row m (the (row, head) pair
+// m0 + m, one contiguous 1152-byte vector) is laid out like KV token m, so the
+// QK B-operand fragments are read exactly like K fragments. The block's pairs
+// are contiguous in q, so these are the same 1 KB direct loads as a KV tile:
+// about half the bytes of per-wave register loads (each row group's two waves
+// need the same rows) and no partial-line requests. Pairs past the request's
+// last one read the zero row.
+__device__ __forceinline__ void issue_q_tile(const AttnArgs& a, const WorkUnit& u,
+                                             unsigned char* dst, int wave, int lane,
+                                             const unsigned char* zero) {
+  const unsigned char* qb =
+      reinterpret_cast<const unsigned char*>(a.q + ((int64_t)u.qs * a.H + u.m0) * kHeadDim);
+  auto src_of = [&](int row) -> const unsigned char* {
+    return u.m0 + row < u.M ? qb + (int64_t)row * kTokBytesBf16 : zero;
+  };
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const uint16_t* qp =
-        a.q + ((int64_t)u.qs * a.H + (row_ok[rt] ? mrow[rt] : 0)) * kHeadDim + 8 * g4;
+  for (int j = 0; j < 16; ++j) {
+    const int row = 16 * wave + j;
+    dma16(src_of(row) + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
+  }
 #pragma unroll
-    for (int k = 0; k < kQSteps; ++k) {
-      uint4 v = row_ok[rt] ? *reinterpret_cast<const uint4*>(qp + 32 * k) : make_uint4(0, 0, 0, 0);
-      qf[rt][k] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int jj = 0; jj < 2; ++jj) {
+    const int uu = lane >> 3;
+    const int chunk = (lane & 7) ^ uu;
+    const int row = 16 * wave + 8 * jj + uu;
+    dma16(src_of(row) + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
   }
 }
 
@@ -252,6 +294,37 @@ __device__ __forceinline__ bf16x8 k_fragment(const unsigned char* tile, int tok,
   const int chunk = 4 * (k - kLatQSteps) + g4;
   return *reinterpret_cast<const bf16x8*>(tile + kLatBytes + tok * kRopeRow +
                                           16 * (chunk ^ (tok & 7)));
+}
+
+// Q fragments (B operand of S^T = K Q^T) of this lane's rows from the staged
+// Q tile: 8 dims per lane per K-step. The reads are inline assembly that lands
+// them in accumulation registers, where the MFMAs take them as operands
+// directly (the compiler would otherwise keep them there and copy each one
+// back before every use); the trailing wait is tied to every fragment.
+__device__ __forceinline__ void read_q(const unsigned char* qtile, int g, int lane,
+                                       bf16x8 (&qf)[2][kQSteps]) {
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = 32 * g + 16 * rt + (lane & 15);
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
+      const unsigned char* p =
+          k < kLatQSteps ? qtile + lat_off(row, 4 * k + g4)
+                         : qtile + kLatBytes + row * kRopeRow +
+                               16 * ((4 * (k - kLatQSteps) + g4) ^ (row & 7));
+      const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
+      asm volatile("ds_read_b128 %0, %1" : "=a"(qf[rt][k]) : "v"(addr));
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int k = 0; k < kQSteps; k += 6)
+      asm volatile("" : "+a"(qf[rt][k]), "+a"(qf[rt][k + 1]), "+a"(qf[rt][k + 2]),
+                        "+a"(qf[rt][k + 3]), "+a"(qf[rt][k + 4]), "+a"(qf[rt][k + 5]));
+  }
 }
 
 // ---------------------------------------------------------------------------

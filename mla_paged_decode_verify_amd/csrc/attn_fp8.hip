@@ -41,7 +41,8 @@ struct Fp8Stage {
   }
   __device__ inline void load(const AttnArgs& a, const unsigned char* pool, int tb, int hi,
                               int wave, int lane) {
-    const unsigned char* src = token_src<kHeadDim>(a, pool, sp, tb + lane, hi) + 16 * kLoads * wave;
+    const unsigned char* src =
+        token_src<kHeadDim>(a, pool, sp, tb + lane, hi, zero_row()) + 16 * kLoads * wave;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) reg[j] = *reinterpret_cast<const uint4*>(src + 16 * j);
   }
@@ -94,14 +95,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   fs.load(a, pool, lo, hi, wave, lane);
   fs.fetch_page(a, pt_row, lo + kTile, hi, lane);
 
+  // ---- Q through the second tile buffer (first written at the second step)
+  issue_q_tile(a, u, buf1, wave, lane, zero_row());
   int mrow[2], hi_row[2];
   bool row_ok[2];
   lane_rows(a, u, g, r16, mrow, hi_row, row_ok);
-  bf16x8 qf[2][kQSteps];
-  load_q(a, u, mrow, row_ok, g4, qf);
-
   WaveState st;
   state_init(st);
+  MLA_WAIT_VMCNT(0);
+  lds_barrier();
+  bf16x8 qf[2][kQSteps];
+  read_q(buf1, g, lane, qf);
 
   // One tile: widen the staged codes into `cur`, start loading the next tile's
   // codes, then compute on `cur` (last read two tiles ago, before the previous

@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
         }
       }
     };
-    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
+    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue, [] {});
   };
   int kt = 0;
   for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
     step(buf1, buf0, tb + kTile, kt + 1);
   }
 
-  store_partials(a, u, st, rx, mrow, row_ok, g, c, lane);
+  store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);
 }
 
 }  // namespace

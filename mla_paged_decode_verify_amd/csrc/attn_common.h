@@ -379,14 +379,15 @@ __device__ __forceinline__ void state_init(WaveState& st) {
 
 // Scores, softmax and PV for one 64-token tile held in `tile` (LDS).
 // `issue(k)` is called once per QK K-step (k = 0..17), so that the loads of
-// the next tile can be spread over the MFMA work.
-template <class Issue>
+// the next tile can be spread over the MFMA work; `after_qk()` runs once the
+// Q fragments have been used for the last time in this tile.
+template <class Issue, class AfterQK>
 __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ tile,
                                              PExchange* __restrict__ px,
                                              const bf16x8 (&qf)[2][kQSteps],
                                              WaveState& st, int tb, const int (&hi_row)[2],
                                              float qk_scale_log2, int g, int c, int lane,
-                                             Issue&& issue) {
+                                             Issue&& issue, AfterQK&& after_qk) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
 
@@ -417,9 +418,13 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  after_qk();
 
   // ---- scale, mask, row maximum over this wave's 32 tokens. Element e of a
-  // row tile is token 32c + 16(e/4) + 4(l/16) + e%4.
+  // row tile is token 32c + 16(e/4) + 4(l/16) + e%4. Tiles that every row of
+  // the wave sees whole skip the masking.
+  const bool whole =
+      __builtin_amdgcn_ballot_w64(tb + kTile > hi_row[0] || tb + kTile > hi_row[1]) == 0;
   float mx[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -429,7 +434,8 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int tok = tb + 32 * c + 16 * tt + 4 * g4 + v;
-        const float x = tok < hi_row[rt] ? sacc[rt][tt][v] * qk_scale_log2 : kNegInf;
+        const float y = sacc[rt][tt][v] * qk_scale_log2;
+        const float x = whole || tok < hi_row[rt] ? y : kNegInf;
         sacc[rt][tt][v] = x;
         mx[rt] = fmaxf(mx[rt], x);
       }
@@ -440,12 +446,13 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
 
   // ---- V^T reads for the first PV steps go out before the barrier. Lane i of
   // each 16-lane group points at dims 16n + 4(i%4) of token t0 + i/4; the
-  // transposed read hands it dim 16n + i of tokens t0..t0+3. Steps
-  // t = 16kk + n (K-step kk, 16-dim tile n); each step's two reads are issued
-  // three steps ahead of its MFMAs (a 4-slot ring).
+  // transposed read hands it dim 16n + i of tokens t0..t0+3. Step t covers
+  // 16-dim tile n = t % 16 and, for t < 16, the wave's own token half (K-step
+  // of the PV product: tokens 32c..32c+31), for t >= 16 the partner's; each
+  // step's two reads are issued three steps ahead of its MFMAs (a 4-slot ring).
   const int i16 = lane & 15;
   auto vread = [&](int t, i16x4& lo4, i16x4& hi4) {
-    const int kk = t >> 4, n = t & 15;
+    const int kk = t < 16 ? c : c ^ 1, n = t & 15;
     const int row = 32 * kk + 4 * g4 + (i16 >> 2);
     const int ch = 32 * c + 2 * n + ((i16 & 3) >> 1);
     const int byte = 8 * (i16 & 1);
@@ -488,44 +495,50 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
     const float m_use = st.m_ref[rt] == kNegInf ? 0.f : st.m_ref[rt];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = sacc[rt][e >> 2][e & 3];
-      const float p = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x - m_use);
+      // masked: x = -inf and exp2(-inf) = 0 (m_use is finite)
+      const float p = __builtin_amdgcn_exp2f(sacc[rt][e >> 2][e & 3] - m_use);
       st.l_part[rt] += p;
       pown[rt][e] = (__bf16)p;
     }
     px->p[g][c][rt][lane] = __builtin_bit_cast(uint4, pown[rt]);
   }
-  lds_barrier();
-  // K-step kk of the PV product covers tokens 32kk..32kk+31, i.e. half kk
-  bf16x8 pf[2][2];  // [token half][row tile]
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const bf16x8 ppart = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][rt][lane]);
-    pf[0][rt] = c == 0 ? pown[rt] : ppart;
-    pf[1][rt] = c == 0 ? ppart : pown[rt];
-  }
+  // The own half of the PV product needs only this wave's P: it runs while
+  // the partner's P is on its way (the exchange barrier sits at step 16).
+  bf16x8 ppart[2];
 
   // ---- O^T[256 dims x 32 rows] += V^T[256 x 64 tokens] P^T[64 x 32]
 #pragma unroll
   for (int t = 0; t < kPvSteps; ++t) {
+    if (t == 16) {
+      lds_barrier();
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        ppart[rt] = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][rt][lane]);
+    }
     if (t + 3 < kPvSteps) vread(t + 3, vr[(t + 3) % 4][0], vr[(t + 3) % 4][1]);
     __builtin_amdgcn_sched_barrier(0);
-    const int kk = t >> 4, n = t & 15;
+    const int n = t & 15;
     const bf16x8 va = __builtin_bit_cast(
         bf16x8, __builtin_shufflevector(vr[t % 4][0], vr[t % 4][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
-      st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[kk][rt], st.o[rt][n], 0, 0, 0);
+      st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, t < 16 ? pown[rt] : ppart[rt],
+                                                            st.o[rt][n], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // End of the segment: add the partner wave's row sums and write the partials
-// (maximum, sum and O relative to the maximum).
+// (maximum, sum and O relative to the maximum). O goes through LDS (`stage`:
+// this row group's 32 rows, a tile buffer no longer read) so that the global
+// stores write whole rows, 1 KB per instruction, instead of 64-byte pieces.
+constexpr int kStageRow = 4 * kVDim + 16;   // padded: conflict-free row-tile writes
+static_assert(32 * kStageRow <= kBufBytes, "a row group's O fits a tile buffer");
 __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit& u,
                                                const WaveState& st, RowExchange& rx,
-                                               const int (&mrow)[2], const bool (&row_ok)[2],
-                                               int g, int c, int lane) {
+                                               unsigned char* stage, const int (&mrow)[2],
+                                               const bool (&row_ok)[2], int g, int c,
+                                               int lane) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   float l_row[2];
@@ -534,27 +547,37 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
     l_row[rt] = sum4(st.l_part[rt]);
     if (g4 == 0) rx.l[g][c][rt][r16] = l_row[rt];
   }
-  __syncthreads();
+  __syncthreads();                          // also: no wave reads a tile buffer any more
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    if (!row_ok[rt]) continue;
     const float L = l_row[rt] + rx.l[g][c ^ 1][rt][r16];
     // move O and l from the reference exponent to the true maximum
     float fix = 1.f;
     if (st.m_true[rt] != kNegInf) fix = __builtin_amdgcn_exp2f(st.m_ref[rt] - st.m_true[rt]);
     const float vs = fix * a.v_scale;
-    const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow[rt]) * a.nseg + u.s;
-    if (c == 0 && g4 == 0) {
+    if (row_ok[rt] && c == 0 && g4 == 0) {
+      const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow[rt]) * a.nseg + u.s;
       a.segm_max[e] = st.m_true[rt];
       a.segm_expsum[e] = L * fix;
     }
-    float* op = a.segm_out + e * kVDim + 256 * c + 4 * g4;
+    float* sp = reinterpret_cast<float*>(stage + (16 * rt + r16) * kStageRow) + 256 * c + 4 * g4;
 #pragma unroll
-    for (int n = 0; n < kNTiles / 2; ++n) {
-      *reinterpret_cast<float4*>(op + 16 * n) =
-          make_float4(st.o[rt][n][0] * vs, st.o[rt][n][1] * vs, st.o[rt][n][2] * vs,
-                      st.o[rt][n][3] * vs);
-    }
+    for (int n = 0; n < kNTiles / 2; ++n)
+      *reinterpret_cast<f32x4*>(sp + 16 * n) = st.o[rt][n] * vs;
+  }
+  __syncthreads();
+  // wave (g, c) stores rows 16c .. 16c + 15 of its row group, half a row a go
+  const int row0 = u.m0 + 32 * g + 16 * c;
+#pragma unroll 4
+  for (int k = 0; k < 16; ++k) {
+    if (row0 + k >= u.M) break;
+    const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + row0 + k) * a.nseg + u.s;
+    const unsigned char* src = stage + (16 * c + k) * kStageRow + 16 * lane;
+    float* dst = a.segm_out + e * kVDim + 4 * lane;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<float4*>(dst + 256 * h) =
+          *reinterpret_cast<const float4*>(src + 1024 * h);
   }
 }
 

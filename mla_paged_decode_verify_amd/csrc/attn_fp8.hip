@@ -117,14 +117,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
       fs.load(a, pool, tb + kTile, hi, wave, lane);
       fs.fetch_page(a, pt_row, tb + 2 * kTile, hi, lane);
     }
-    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, [](int) {});
+    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, [](int) {}, [] {});
   };
   for (int tb = lo; tb < hi; tb += 2 * kTile) {
     step(buf0, tb);
     if (tb + kTile >= hi) break;
     step(buf1, tb + kTile);
   }
-  store_partials(a, u, st, rx, mrow, row_ok, g, c, lane);
+  store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);
 }
 
 }  // namespace

@@ -133,8 +133,10 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
  *   q          [R, H, 576] bf16 queries (RoPE already applied)
  *   kv         [W, num_blocks, block_size, 576] cache: one pool per shard,
  *              elements bf16 or e4m3fn per kv_dtype; 16-byte aligned
- *   kv_scale   fp8 descale (real = code * kv_scale); ignored for bf16
- *   sm_scale   softmax scale applied to <q, k> (e.g. 1/sqrt(576))
+ *   kv_scale   fp8 descale (real = code * kv_scale), > 0; ignored for bf16
+ *   sm_scale   softmax scale applied to <q, k> (e.g. 1/sqrt(576)), > 0; the
+ *              product sm_scale * kv_scale * log2(e) must be a positive
+ *              finite fp32 value, else MLA_ERR_INVALID
  *   row_lens, page_table, pt_width, page_size: from mla_verify_plan
  *   q_start    [N+1] as given to the plan; max_qlen >= every Q_i
  *   nseg       segments per (request, shard) group. Partition (a reading of

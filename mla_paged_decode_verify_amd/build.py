@@ -29,7 +29,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-source extras. The attention kernels keep their 128-register output
 # accumulators in VGPRs (they rescale them with plain VALU multiplies; AGPR
 # copies would cost 256 moves a tile) and the query fragments in AGPRs.
-_ATTN = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+_ATTN = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
 SOURCE_FLAGS = {"attn_bf16.hip": _ATTN, "attn_fp8.hip": _ATTN}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]

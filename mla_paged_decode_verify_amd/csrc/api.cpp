@@ -136,8 +136,15 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
   if (pt_width < 0) return fail(MLA_ERR_INVALID, "mla_verify_attn: pt_width must be >= 0");
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
     return fail(MLA_ERR_UNSUPPORTED, "mla_verify_attn: unknown kv_dtype %d", (int)kv_dtype);
-  if (!std::isfinite(sm_scale) || (kv_dtype == MLA_KV_FP8_E4M3 && !std::isfinite(kv_scale)))
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: non-finite scale");
+  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  const double log2e = 1.4426950408889634;
+  const float qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)kv_scale : 1.0) * log2e);
+  // the kernels take the row maximum of unscaled scores, which needs a
+  // positive scale that stays positive and finite in fp32
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale) ||
+      (fp8 && (!(kv_scale > 0.f) || !std::isfinite(kv_scale))) || !(qk_scale_log2 > 0.f) ||
+      !std::isfinite(qk_scale_log2))
+    return fail(MLA_ERR_INVALID, "mla_verify_attn: scales must be positive and finite");
   if (!q || !kv || !row_lens || !q_start || !segm_out || !segm_max || !segm_expsum ||
       (pt_width > 0 && !page_table))
     return fail(MLA_ERR_INVALID, "mla_verify_attn: null tensor argument");
@@ -147,7 +154,6 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
   if ((int64_t)N * W * nseg * mblocks > 0x7FFFFFFFLL)
     return fail(MLA_ERR_INVALID, "mla_verify_attn: grid too large");
 
-  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
   mla::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint8_t*>(kv);
@@ -158,8 +164,7 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
   a.row_lens = row_lens; a.page_table = page_table; a.pt_width = pt_width;
   a.q_start = q_start; a.N = N; a.R = R; a.H = H; a.W = W; a.nseg = nseg;
   a.mblocks = (int32_t)mblocks;
-  const double log2e = 1.4426950408889634;
-  a.qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)kv_scale : 1.0) * log2e);
+  a.qk_scale_log2 = qk_scale_log2;
   a.v_scale = fp8 ? kv_scale : 1.0f;
   a.segm_out = segm_out; a.segm_max = segm_max; a.segm_expsum = segm_expsum;
   return hip_status(mla::launch_attn(a, fp8, (hipStream_t)stream), "mla_verify_attn launch");

@@ -34,10 +34,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   __shared__ __align__(16) unsigned char buf1[kBufBytes];
   __shared__ PExchange px;
   __shared__ RowExchange rx;
-  const WorkUnit u = decode_unit(a, blockIdx.x);
+  WorkUnit u = decode_head(a, blockIdx.x);
   if (!u.valid) return;
-  const int lo = u.lo, hi = u.hi;
-  if (lo >= hi) return;                     // segment inactive for the whole group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -51,7 +49,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   const unsigned char* zero = zero_row();
   const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
 
-  // ---- first tile in flight before anything else
+  // ---- Q first (it needs only the request's rows), through the second tile
+  // buffer: free until the first step's barrier, after which the next tile's
+  // loads target it
+  issue_q_tile(a, u, buf1, wave, lane, zero);
+  decode_tail(a, u);
+  const int lo = u.lo, hi = u.hi;
+  if (lo >= hi) {                           // segment inactive for the whole group:
+    MLA_WAIT_VMCNT(0);                      // let the Q loads land before the LDS is released
+    return;
+  }
+
+  // ---- first tile
   int32_t vpg = 0;                          // SLICE: pages of tiles 64q .. 64q + 63
   Bf16Pages pg;
   if constexpr (SLICE) {
@@ -64,9 +73,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
     issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane, zero);
   }
 
-  // ---- Q through the second tile buffer (free until the first tile's loads
-  // of the next tile, which come after the first step's barrier)
-  issue_q_tile(a, u, buf1, wave, lane, zero);
   int mrow[2], hi_row[2];
   bool row_ok[2];
   lane_rows(a, u, g, r16, mrow, hi_row, row_ok);

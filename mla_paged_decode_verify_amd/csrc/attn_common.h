@@ -216,7 +216,7 @@ struct WorkUnit {
 // block) get consecutive ids on that XCD, so they run side by side: its Q,
 // and each unit's KV across row blocks, come from HBM into that XCD's L2
 // once. The grid covers ceil(N / 8) * 8 requests.
-__device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
+__device__ inline WorkUnit decode_head(const AttnArgs& a, int b) {
   WorkUnit u;
   const int slot = b >> 3;
   u.mb = slot % a.mblocks;
@@ -234,13 +234,20 @@ __device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
   u.m0 = u.mb * kAttnRows;
   u.valid = !(u.qs < 0 || u.Q <= 0 || u.qs + u.Q > a.R || u.m0 >= u.M);
   u.last = u.qs + u.Q - 1;                  // the group's longest row
-  u.lo = u.hi = 0;
-  if (!u.valid) return u;
+  return u;
+}
+// The unit's segment [lo, hi) from the group's longest row (lo >= hi: the
+// segment holds no tokens of this group).
+__device__ inline void decode_tail(const AttnArgs& a, WorkUnit& u) {
   int Lg = a.row_lens[(int64_t)u.r * a.R + u.last];
   Lg = min(Lg, a.pt_width * a.page_size);
   const int span = (Lg + a.nseg * a.page_size - 1) / (a.nseg * a.page_size) * a.page_size;
   u.lo = u.s * span;
-  u.hi = min(u.lo + span, Lg);             // lo >= hi: segment inactive for the group
+  u.hi = min(u.lo + span, Lg);
+}
+__device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
+  WorkUnit u = decode_head(a, b);
+  if (u.valid) decode_tail(a, u);
   return u;
 }
 
@@ -392,20 +399,21 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
   const int g4 = lane >> 4;
 
   // ---- S^T[32 tokens x 32 rows]: per K-step two K fragments (16 tokens each),
-  // each feeding both row tiles. Fragments are read two K-steps ahead of their
-  // MFMAs (a 3-slot ring); the scheduling barriers keep that order.
+  // each feeding both row tiles. Fragments are read kKAhead K-steps ahead of
+  // their MFMAs (a ring); the scheduling barriers keep that order.
+  constexpr int kKAhead = 2;
   f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};  // [row tile][token tile]
-  bf16x8 kr[3][2];
+  bf16x8 kr[kKAhead + 1][2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kKAhead; ++k) {
     kr[k][0] = k_fragment(tile, 32 * c + r16, k, g4);
     kr[k][1] = k_fragment(tile, 32 * c + 16 + r16, k, g4);
   }
 #pragma unroll
   for (int k = 0; k < kQSteps; ++k) {
-    if (k + 2 < kQSteps) {
-      kr[(k + 2) % 3][0] = k_fragment(tile, 32 * c + r16, k + 2, g4);
-      kr[(k + 2) % 3][1] = k_fragment(tile, 32 * c + 16 + r16, k + 2, g4);
+    if (k + kKAhead < kQSteps) {
+      kr[(k + kKAhead) % (kKAhead + 1)][0] = k_fragment(tile, 32 * c + r16, k + kKAhead, g4);
+      kr[(k + kKAhead) % (kKAhead + 1)][1] = k_fragment(tile, 32 * c + 16 + r16, k + kKAhead, g4);
     }
     issue(k);
     __builtin_amdgcn_sched_barrier(0);
@@ -413,33 +421,36 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k % 3][tt], qf[rt][k],
+        sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k % (kKAhead + 1)][tt], qf[rt][k],
                                                                sacc[rt][tt], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   after_qk();
 
-  // ---- scale, mask, row maximum over this wave's 32 tokens. Element e of a
-  // row tile is token 32c + 16(e/4) + 4(l/16) + e%4. Tiles that every row of
-  // the wave sees whole skip the masking.
-  const bool whole =
-      __builtin_amdgcn_ballot_w64(tb + kTile > hi_row[0] || tb + kTile > hi_row[1]) == 0;
+  // ---- mask, row maximum over this wave's 32 tokens. Element e of a row tile
+  // is token 32c + 16(e/4) + 4(l/16) + e%4. Tiles that every row of the wave
+  // sees whole skip the masking. The scores stay unscaled: the scale is
+  // positive, so the maximum of the rounded scaled scores is the rounded
+  // scaled maximum, and the scale goes into the exponent's fused multiply-add.
+  if (__builtin_amdgcn_ballot_w64(tb + kTile > hi_row[0] || tb + kTile > hi_row[1]) != 0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = tb + 32 * c + 16 * tt + 4 * g4 + v;
+          if (tok >= hi_row[rt]) sacc[rt][tt][v] = kNegInf;
+        }
+      }
+    }
+  }
   float mx[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    mx[rt] = kNegInf;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = tb + 32 * c + 16 * tt + 4 * g4 + v;
-        const float y = sacc[rt][tt][v] * qk_scale_log2;
-        const float x = whole || tok < hi_row[rt] ? y : kNegInf;
-        sacc[rt][tt][v] = x;
-        mx[rt] = fmaxf(mx[rt], x);
-      }
-    }
+    mx[rt] = fmaxf(fmaxf(fmaxf(sacc[rt][0][0], sacc[rt][0][1]), fmaxf(sacc[rt][0][2], sacc[rt][0][3])),
+                   fmaxf(fmaxf(sacc[rt][1][0], sacc[rt][1][1]), fmaxf(sacc[rt][1][2], sacc[rt][1][3])));
     mx[rt] = max4(mx[rt]);
     if (g4 == 0) px->mx[g][c][rt][r16] = mx[rt];
   }
@@ -449,7 +460,7 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
   // transposed read hands it dim 16n + i of tokens t0..t0+3. Step t covers
   // 16-dim tile n = t % 16 and, for t < 16, the wave's own token half (K-step
   // of the PV product: tokens 32c..32c+31), for t >= 16 the partner's; each
-  // step's two reads are issued three steps ahead of its MFMAs (a 4-slot ring).
+  // step's two reads are issued kVAhead steps ahead of its MFMAs (a ring).
   const int i16 = lane & 15;
   auto vread = [&](int t, i16x4& lo4, i16x4& hi4) {
     const int kk = t < 16 ? c : c ^ 1, n = t & 15;
@@ -461,15 +472,16 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
         (lds_i16x4*)(tile + lat_off(row + 16, ch) + byte));
   };
   constexpr int kPvSteps = 2 * (kNTiles / 2);
-  i16x4 vr[4][2];
+  constexpr int kVAhead = 3;
+  i16x4 vr[kVAhead + 1][2];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) vread(t, vr[t][0], vr[t][1]);
+  for (int t = 0; t < kVAhead; ++t) vread(t, vr[t][0], vr[t][1]);
 
   lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     // the partner saw the other 32 tokens; both waves now hold the same tile max
-    mx[rt] = fmaxf(mx[rt], px->mx[g][c ^ 1][rt][r16]);
+    mx[rt] = fmaxf(mx[rt], px->mx[g][c ^ 1][rt][r16]) * qk_scale_log2;
     st.m_true[rt] = fmaxf(st.m_true[rt], mx[rt]);
   }
 
@@ -495,8 +507,9 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
     const float m_use = st.m_ref[rt] == kNegInf ? 0.f : st.m_ref[rt];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // masked: x = -inf and exp2(-inf) = 0 (m_use is finite)
-      const float p = __builtin_amdgcn_exp2f(sacc[rt][e >> 2][e & 3] - m_use);
+      // masked: the score is -inf and exp2(-inf) = 0 (m_use is finite)
+      const float p =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rt][e >> 2][e & 3], qk_scale_log2, -m_use));
       st.l_part[rt] += p;
       pown[rt][e] = (__bf16)p;
     }
@@ -515,11 +528,13 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
       for (int rt = 0; rt < 2; ++rt)
         ppart[rt] = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][rt][lane]);
     }
-    if (t + 3 < kPvSteps) vread(t + 3, vr[(t + 3) % 4][0], vr[(t + 3) % 4][1]);
+    if (t + kVAhead < kPvSteps)
+      vread(t + kVAhead, vr[(t + kVAhead) % (kVAhead + 1)][0], vr[(t + kVAhead) % (kVAhead + 1)][1]);
     __builtin_amdgcn_sched_barrier(0);
     const int n = t & 15;
     const bf16x8 va = __builtin_bit_cast(
-        bf16x8, __builtin_shufflevector(vr[t % 4][0], vr[t % 4][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        bf16x8, __builtin_shufflevector(vr[t % (kVAhead + 1)][0], vr[t % (kVAhead + 1)][1], 0, 1, 2,
+                                        3, 4, 5, 6, 7));
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
       st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, t < 16 ? pown[rt] : ppart[rt],

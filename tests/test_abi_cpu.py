@@ -96,6 +96,10 @@ def _attn(**over):
     (dict(kv_dtype=7), _lib.MLA_ERR_UNSUPPORTED),
     (dict(sm_scale=float("nan")), _lib.MLA_ERR_INVALID),
     (dict(kv_dtype=1, kv_scale=float("inf")), _lib.MLA_ERR_INVALID),
+    (dict(sm_scale=0.0), _lib.MLA_ERR_INVALID),
+    (dict(sm_scale=-0.04), _lib.MLA_ERR_INVALID),
+    (dict(kv_dtype=1, kv_scale=-1.0), _lib.MLA_ERR_INVALID),
+    (dict(kv_dtype=1, kv_scale=1e-40, sm_scale=1e-10), _lib.MLA_ERR_INVALID),
     (dict(q=None), _lib.MLA_ERR_INVALID),
     (dict(q=FAKE + 2), _lib.MLA_ERR_INVALID),
     (dict(max_qlen=0), _lib.MLA_ERR_INVALID),

@@ -5,7 +5,12 @@ One step = plan (row lengths + sub-page tables) -> split-K attention partials
 -> segment + shard LSE merge, over one batch of the workload, inputs resident
 in HBM. The KV cache is rotated over several copies (more than the 256 MB
 Infinity Cache holds) so that no step re-reads the previous step's KV from
-cache. Prints one JSON line.
+cache. Timed steps launch the three calls from Python; --graph replays a HIP
+graph of them instead (one graph per KV copy; on this stack a replay costs more
+launch overhead than the eager calls).
+`eager_split_us` splits eager steps with events (host launch gaps included);
+the attention kernel's own duration comes from back-to-back launches.
+Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload verify_dcp8]
 """
@@ -36,6 +41,9 @@ def parse():
     ap.add_argument("--nseg", type=int, default=None)
     ap.add_argument("--kv-copies", type=int, default=0,
                     help="KV copies to rotate over (0: enough for > 512 MB)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a HIP graph of each step's three launches instead of "
+                         "launching them from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -134,7 +142,7 @@ def main():
     i32 = dict(dtype=torch.int32, device="cuda")
     plan_bufs = dict(row_lens=torch.empty((W, R), **i32),
                      page_table=torch.empty((W, R, ptw), **i32),
-                     qo_indptr=torch.empty((R + 1,), **i32), err_flag=torch.empty((1,), **i32))
+                     qo_indptr=torch.empty((R + 1,), **i32), err_flag=torch.zeros((1,), **i32))
     f32 = dict(dtype=torch.float32, device="cuda")
     parts = (torch.empty((W, R, H, nseg, 512), **f32), torch.empty((W, R, H, nseg), **f32),
              torch.empty((W, R, H, nseg), **f32))
@@ -171,11 +179,42 @@ def main():
     torch.cuda.synchronize()
     if int(plan_bufs["err_flag"].item()) != 0:
         raise SystemExit(f"plan reported errors: {int(plan_bufs['err_flag'].item())}")
-    t0 = time.perf_counter()
+    # Per-kernel split of a step: eager steps bracketed by events.
     for k in range(args.steps):
         step(k, ev[k])
     torch.cuda.synchronize()
+    plan_ms = np.mean([e[0].elapsed_time(e[1]) for e in ev])
+    attn_ms = np.mean([e[1].elapsed_time(e[2]) for e in ev])
+    merge_ms = np.mean([e[2].elapsed_time(e[3]) for e in ev])
+    # The timed steps: the eager calls, or one HIP graph per KV copy holding
+    # the step's three launches.
+    graphs = []
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(len(kvs)):
+                step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in range(len(kvs)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for k in range(args.warmup):
+            graphs[k % len(graphs)].replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if graphs:
+            graphs[k % len(graphs)].replay()
+        else:
+            step(k)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if int(plan_bufs["err_flag"].item()) != 0:
+        raise SystemExit(f"plan reported errors: {int(plan_bufs['err_flag'].item())}")
     # The attention kernel's average launch duration: back-to-back launches on
     # the same stream (the plan is already in place), bracketed by two events.
     n_attn = 20
@@ -190,9 +229,6 @@ def main():
     a1.record()
     torch.cuda.synchronize()
     attn_launch_ms = a0.elapsed_time(a1) / n_attn
-    plan_ms = np.mean([e[0].elapsed_time(e[1]) for e in ev])
-    attn_ms = np.mean([e[1].elapsed_time(e[2]) for e in ev])
-    merge_ms = np.mean([e[2].elapsed_time(e[3]) for e in ev])
     ms_step = wall * 1e3 / args.steps
     achieved = kv_bytes / (attn_launch_ms * 1e-3) / 1e9
     res = {
@@ -211,7 +247,8 @@ def main():
                    "kv_copies": len(kvs)},
         "rows_per_s": round(R / (ms_step * 1e-3), 1),
         "hbm_frac": round(kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "kernel_us": {"plan": round(plan_ms * 1e3, 2), "attn": round(attn_ms * 1e3, 2),
+        "launch": "hip_graph" if args.graph else "eager",
+        "eager_split_us": {"plan": round(plan_ms * 1e3, 2), "attn": round(attn_ms * 1e3, 2),
                       "merge": round(merge_ms * 1e3, 2),
                       "attn_back_to_back": round(attn_launch_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

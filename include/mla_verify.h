@@ -56,7 +56,7 @@ typedef enum {
 #define MLA_HEAD_DIM 576
 #define MLA_V_DIM 512
 
-/* Device error bits written to *err_flag by mla_verify_plan. A request with
+/* Device error bits ORed into *err_flag by mla_verify_plan. A request with
  * any of these problems gets row length 0 on every shard and an all -1
  * sub-page table, so later calls never read outside the caller's buffers. */
 #define MLA_PLAN_ERR_QLEN 1u    /* Q_i < 1, S_i < Q_i, or q_start not monotone  */
@@ -113,8 +113,11 @@ size_t mla_verify_workspace_bytes(int32_t W, int32_t R, int32_t H, int32_t nseg)
  *   page_table  [W, R, pt_width] int32 sub-page ids; entry k < ceil(L/P) is
  *               block_table[i][k*P / B] * (B/P) + (k*P % B) / P, the rest -1
  *   qo_indptr   [R+1] int32 = 0..R (one query per row); may be NULL
- *   err_flag    [1] uint32, may be NULL: set to the OR of MLA_PLAN_ERR_* bits
- *               (0 when every request is valid)
+ *   err_flag    [1] uint32, may be NULL: the MLA_PLAN_ERR_* bits of every
+ *               invalid request are ORed into it. The library never clears
+ *               it (sticky, like a device error flag): a caller zeroes it
+ *               once and again after handling an error; it then stays 0 as
+ *               long as every request of every call is valid.
  */
 mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
                              const int32_t* q_start, int32_t R, int32_t W,

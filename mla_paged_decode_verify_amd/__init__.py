@@ -73,7 +73,8 @@ def mla_verify_plan(seq_lens, q_start, R, W, block_table, num_blocks, block_size
                     row_lens=None, page_table=None, qo_indptr=None, err_flag=None,
                     stream=None):
     """Row lengths [W, R], sub-page table [W, R, pt_width], qo_indptr [R+1] and
-    the device error word (int32 view of the uint32 MLA_PLAN_ERR_* bits).
+    the device error word (int32 view of the uint32 MLA_PLAN_ERR_* bits; sticky:
+    bits are ORed in and never cleared, and a word allocated here starts at 0).
     seq_lens [N], q_start [N+1] and block_table [N, max_blocks] are int32
     device tensors; R = q_start[N] is passed by the caller (no device read)."""
     _dev(seq_lens, torch.int32, "seq_lens")
@@ -96,7 +97,7 @@ def mla_verify_plan(seq_lens, q_start, R, W, block_table, num_blocks, block_size
     if qo_indptr is None:
         qo_indptr = torch.empty((R + 1,), dtype=torch.int32, device=dev)
     if err_flag is None:
-        err_flag = torch.empty((1,), dtype=torch.int32, device=dev)
+        err_flag = torch.zeros((1,), dtype=torch.int32, device=dev)  # sticky: starts clear
     for t, n in ((row_lens, "row_lens"), (page_table, "page_table"),
                  (qo_indptr, "qo_indptr"), (err_flag, "err_flag")):
         _dev(t, torch.int32, n)

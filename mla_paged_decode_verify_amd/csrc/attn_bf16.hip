@@ -43,7 +43,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   const int g = wave >> 1;                  // row group: 32 rows
   const int c = wave & 1;                   // token half (QK) / latent half (PV)
   const int r16 = lane & 15;
-  const int g4 = lane >> 4;
 
   const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kTokBytesBf16;
   const unsigned char* zero = zero_row();

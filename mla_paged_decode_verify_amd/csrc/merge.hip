@@ -9,14 +9,16 @@
 // through the DCP attention merge) and SGLang PR #34432 report, review item 4
 // (natural-log LSE, so the combine uses exp/log).
 //
-// One wave per (row, head) pair. The wave first works on the per-segment
-// statistics with one lane per (shard, segment) -- per-shard maxima, sums and
-// LSEs, the weight of every segment inside its shard and of every shard in the
-// result -- through a small LDS area; then each lane owns 8 consecutive latent
-// dims and streams the partial outputs, all shards' loads in flight at once.
-// Every per-shard output is rounded to bf16 first, as it would be when a shard
-// sends it to the others. Pairs whose W * (nseg + 2) values do not fit the LDS
-// area take a sequential path over shards.
+// One wave per (row, head) pair, in three rounds of global loads: (1) every
+// segment's maximum and sum, this row's length per shard, and the search for
+// the row's request; (2) the length of the request's last row per shard,
+// which fixes the segment partition; (3) the partial outputs, each lane owning
+// 8 consecutive latent dims, several segments in flight at once. Statistics go
+// through a small LDS area: per-shard maxima, sums and LSEs, the weight of
+// every segment inside its shard and of every shard in the result. Every
+// per-shard output is rounded to bf16 first, as it would be when a shard sends
+// it to the others. Pairs whose 2 W (nseg + 1) values do not fit the LDS area
+// take a sequential path over shards.
 #include "internal.h"
 
 namespace mla {
@@ -27,20 +29,30 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kMergeWaves = 4;
 constexpr int kStatSlots = 1024;            // floats of LDS per wave
 
-// Request owning row rho: the largest i with q_start[i] <= rho, by a 64-way
-// search (each round, every lane tests one candidate boundary).
-__device__ inline int find_request(const int32_t* q_start, int N, int rho, int lane) {
+// Request owning row rho and its last row: i with q_start[i] <= rho <
+// q_start[i + 1]. Coarse rounds narrow the range 64 candidates at a time; in
+// the final round lanes 0..n hold q_start[lo .. lo + n], so q_start[i + 1]
+// comes from a lane instead of another load. Returns -1 for a malformed
+// q_start.
+__device__ inline int find_request(const int32_t* q_start, int N, int rho, int lane, int& last) {
   int lo = 0, n = N;                        // answer in [lo, lo + n)
-  while (n > 1) {
+  while (n > 63) {
     const int step = (n + 63) / 64;
     const int cand = lo + lane * step;
     const bool le = cand < lo + n && q_start[cand] <= rho;
     const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
-    if (cnt == 0) return lo;                // malformed q_start; caught below
+    if (cnt == 0) return -1;
     lo += (cnt - 1) * step;
     n = min(step, N - lo);
   }
-  return lo;
+  const int qv = lane <= n ? q_start[lo + lane] : 0x7FFFFFFF;
+  const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(qv <= rho));
+  if (cnt == 0 || cnt > n) return -1;
+  const int first = __builtin_amdgcn_readlane(qv, cnt - 1);
+  const int next = __builtin_amdgcn_readlane(qv, cnt);
+  if (first > rho || next <= rho) return -1;  // not non-decreasing
+  last = next - 1;
+  return lo + cnt - 1;
 }
 
 __device__ inline float bf16_round(float x) { return (float)(__bf16)x; }
@@ -62,15 +74,14 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// Number of segments of shard r that hold tokens of row rho: the attention
-// kernel splits the group's longest row Lg into segments of `span` tokens.
-__device__ inline int active_segments(const MergeArgs& a, int r, int rho, int last) {
-  const int seg_tokens = a.nseg * a.page_size;
-  const int Lg = a.row_lens[(int64_t)r * a.R + last];
-  const int L = a.row_lens[(int64_t)r * a.R + rho];
-  const int span = (Lg + seg_tokens - 1) / seg_tokens * a.page_size;
+// Segments of a row of length L that hold tokens, in a group whose longest
+// row is Lg: the attention kernel cut the group into segments of `span`
+// tokens.
+__device__ inline int active_segments(int Lg, int L, int nseg, int page_size) {
+  const int seg_tokens = nseg * page_size;
+  const int span = (Lg + seg_tokens - 1) / seg_tokens * page_size;
   const int nact = span > 0 ? (L + span - 1) / span : 0;
-  return min(nact, a.nseg);
+  return min(nact, nseg);
 }
 
 __device__ inline void store_out(const MergeArgs& a, int64_t pair, int lane, const float (&v)[8],
@@ -92,12 +103,23 @@ __device__ inline void store_shard(const MergeArgs& a, int r, int rho, int h, in
   if (a.shard_lse != nullptr && lane == 0) a.shard_lse[e] = lse_r;
 }
 
-// Accumulate 8 dims of one partial output with weight c.
-__device__ inline void axpy8(float (&acc)[8], float c, const float* src) {
+// o += c * (8 dims of one partial output); c == 0 marks a segment without
+// tokens, whose memory may never have been written, so its values are
+// discarded rather than multiplied.
+__device__ inline void axpy8(float (&o)[8], float c, const float* src) {
   const float4 x = reinterpret_cast<const float4*>(src)[0];
   const float4 y = reinterpret_cast<const float4*>(src)[1];
-  acc[0] += c * x.x; acc[1] += c * x.y; acc[2] += c * x.z; acc[3] += c * x.w;
-  acc[4] += c * y.x; acc[5] += c * y.y; acc[6] += c * y.z; acc[7] += c * y.w;
+  const bool on = c != 0.f;
+  o[0] += on ? c * x.x : 0.f; o[1] += on ? c * x.y : 0.f;
+  o[2] += on ? c * x.z : 0.f; o[3] += on ? c * x.w : 0.f;
+  o[4] += on ? c * y.x : 0.f; o[5] += on ? c * y.y : 0.f;
+  o[6] += on ? c * y.z : 0.f; o[7] += on ? c * y.w : 0.f;
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
@@ -108,43 +130,53 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
   if (pair >= (int64_t)a.R * a.H) return;
   const int rho = (int)(pair / a.H);
   const int h = (int)(pair % a.H);
-  const int i = find_request(a.q_start, a.N, rho, lane);
-  const int last = a.q_start[i + 1] - 1;
-  if (a.q_start[i] > rho || last < rho || last >= a.R) return;  // malformed q_start
-  const int W = a.W, nseg = a.nseg;
-  float* sl = stat[wave];                   // [W] shard LSEs
-  float* sw = sl + W;                       // [W] shard weights
-  float* sc = sw + W;                       // [W * nseg] segment weights inside a shard
-  const bool fast = W * (nseg + 2) <= kStatSlots;
+  const int W = a.W, nseg = a.nseg, F = W * nseg;
+  // partial index e = r * rstride + pbase + s
+  const int64_t rstride = (int64_t)a.R * a.H * nseg;
+  const int64_t pbase = ((int64_t)rho * a.H + h) * nseg;
 
   float res[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) res[k] = 0.f;
   float lse_out = kNegInf;
 
-  if (fast) {
-    // ---- per shard (one lane each): maximum, sum, LSE and segment weights
+  if (2 * (F + W) <= kStatSlots) {
+    float* sm = stat[wave];                 // [F] segment maxima
+    float* sc = sm + F;                     // [F] segment sums, then segment weights
+    float* sl = sc + F;                     // [W] shard LSEs
+    float* sw = sl + W;                     // [W] shard weights
+    // ---- first round of loads: all that does not depend on the request
+    // (every segment's statistics, whether it holds tokens or not; this row's
+    // length in the first 64 shards), in flight together with the search
+    for (int f = lane; f < F; f += 64) {
+      const int r = f / nseg, s = f - r * nseg;
+      sm[f] = a.segm_max[r * rstride + pbase + s];
+      sc[f] = a.segm_expsum[r * rstride + pbase + s];
+    }
+    const int L0 = lane < W ? a.row_lens[(int64_t)lane * a.R + rho] : 0;
+    int last = 0;
+    if (find_request(a.q_start, a.N, rho, lane, last) < 0 || last >= a.R) return;  // malformed
+    wave_lds_sync();
+
+    // ---- per shard (one lane each): active segments (second round: the
+    // group's longest row), maximum, sum, LSE and segment weights
     float gm = kNegInf;                     // largest LSE of this lane's shards
     for (int r = lane; r < W; r += 64) {
-      const int nact = active_segments(a, r, rho, last);
-      const int64_t base = (((int64_t)r * a.R + rho) * a.H + h) * nseg;
+      const int L = r < 64 ? L0 : a.row_lens[(int64_t)r * a.R + rho];
+      const int Lg = a.row_lens[(int64_t)r * a.R + last];
+      const int nact = active_segments(Lg, L, nseg, a.page_size);
+      float* m = sm + r * nseg;
+      float* c = sc + r * nseg;
       float M = kNegInf;
-      for (int s = 0; s < nact; ++s) M = fmaxf(M, a.segm_max[base + s]);
+      for (int s = 0; s < nact; ++s) M = fmaxf(M, m[s]);
       float E = 0.f;
-      for (int s = 0; s < nact; ++s) {
-        const float sc_s = __builtin_amdgcn_exp2f(a.segm_max[base + s] - M);
-        sc[r * nseg + s] = sc_s;
-        E += a.segm_expsum[base + s] * sc_s;
-      }
-      for (int s = nact; s < nseg; ++s) sc[r * nseg + s] = 0.f;
-      float l = kNegInf;
-      if (M != kNegInf && E > 0.f) {
-        const float inv = 1.f / E;
-        for (int s = 0; s < nact; ++s) sc[r * nseg + s] *= inv;
-        l = kLn2 * (M + __log2f(E));
-      } else {
-        for (int s = 0; s < nact; ++s) sc[r * nseg + s] = 0.f;
-      }
+      if (M != kNegInf)
+        for (int s = 0; s < nact; ++s) E += c[s] * __builtin_amdgcn_exp2f(m[s] - M);
+      const bool live = M != kNegInf && E > 0.f;
+      const float inv = live ? 1.f / E : 0.f;
+      for (int s = 0; s < nseg; ++s)
+        c[s] = live && s < nact ? __builtin_amdgcn_exp2f(m[s] - M) * inv : 0.f;
+      const float l = live ? kLn2 * (M + __log2f(E)) : kNegInf;
       gm = fmaxf(gm, l);
       sl[r] = l;
     }
@@ -164,43 +196,55 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
     } else {
       for (int r = lane; r < W; r += 64) sw[r] = 0.f;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
 
-    // ---- outputs: each lane's 8 dims, shard by shard (bf16 per shard); the
-    // unrolled loop keeps several shards' loads in flight
-#pragma unroll 8
-    for (int r = 0; r < W; ++r) {
-      const int64_t base = (((int64_t)r * a.R + rho) * a.H + h) * nseg;
-      float o[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = 0.f;
-      const float* src = a.segm_out + base * kVDim + 8 * lane;
-#pragma unroll 4
-      for (int s = 0; s < nseg; ++s) {
-        const float c = sc[r * nseg + s];   // 0 for segments without tokens
-        if (c != 0.f) axpy8(o, c, src + (int64_t)s * kVDim);
-      }
+    // ---- outputs (third round): each lane's 8 dims, shard by shard (bf16
+    // per shard); loads are unconditional so that unrolled iterations keep
+    // several segments in flight
+    const float* src = a.segm_out + pbase * kVDim + 8 * lane;
+    const bool want_shard = a.shard_out != nullptr || a.shard_lse != nullptr;
+    auto finish_shard = [&](int r, float (&o)[8]) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = bf16_round(o[k]);
       const float wr = sw[r];
 #pragma unroll
       for (int k = 0; k < 8; ++k) res[k] += wr * o[k];
-      if (a.shard_out != nullptr || a.shard_lse != nullptr) store_shard(a, r, rho, h, lane, o, sl[r]);
+      if (want_shard) store_shard(a, r, rho, h, lane, o, sl[r]);
+    };
+    if (nseg == 1) {
+#pragma unroll 4
+      for (int r = 0; r < W; ++r) {
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = 0.f;
+        axpy8(o, sc[r], src + r * rstride * kVDim);
+        finish_shard(r, o);
+      }
+    } else {
+      for (int r = 0; r < W; ++r) {
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = 0.f;
+#pragma unroll 4
+        for (int s = 0; s < nseg; ++s) axpy8(o, sc[r * nseg + s], src + (r * rstride + s) * kVDim);
+        finish_shard(r, o);
+      }
     }
     store_out(a, pair, lane, res, lse_out);
     return;
   }
 
   // ---- sequential path: shards folded in online
+  int last = 0;
+  if (find_request(a.q_start, a.N, rho, lane, last) < 0 || last >= a.R) return;  // malformed
   float gmax = kNegInf, gsum = 0.f;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
   for (int r = 0; r < W; ++r) {
-    const int nact = active_segments(a, r, rho, last);
-    const int64_t base = (((int64_t)r * a.R + rho) * a.H + h) * nseg;
+    const int nact = active_segments(a.row_lens[(int64_t)r * a.R + last],
+                                     a.row_lens[(int64_t)r * a.R + rho], nseg, a.page_size);
+    const int64_t base = r * rstride + pbase;
     float M = kNegInf;
     for (int s = 0; s < nact; ++s) M = fmaxf(M, a.segm_max[base + s]);
     float o[8];
@@ -214,10 +258,15 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
         E += a.segm_expsum[base + s] * c;
         axpy8(o, c, a.segm_out + (base + s) * kVDim + 8 * lane);
       }
-      const float inv = 1.f / E;
+      if (E > 0.f) {
+        const float inv = 1.f / E;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = bf16_round(o[k] * inv);
-      lse_r = kLn2 * (M + __log2f(E));
+        for (int k = 0; k < 8; ++k) o[k] = bf16_round(o[k] * inv);
+        lse_r = kLn2 * (M + __log2f(E));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = 0.f;
+      }
     }
     store_shard(a, r, rho, h, lane, o, lse_r);
     if (lse_r == kNegInf) continue;          // empty shard contributes nothing

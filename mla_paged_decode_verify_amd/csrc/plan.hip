@@ -10,16 +10,15 @@
 //
 // One workgroup per request: it checks the request (the block ids it uses are
 // checked by all threads at once), then writes the request's row lengths and
-// table cells for every shard. A one-thread kernel clears the error word
-// first, since every workgroup ORs its bits into it.
+// table cells for every shard. Error bits are ORed into the caller's error
+// word, which the library never clears (a sticky flag), so a valid batch
+// costs no extra launch.
 #include "internal.h"
 
 namespace mla {
 namespace {
 
 constexpr int kPlanThreads = 256;
-
-__global__ void plan_clear_kernel(uint32_t* err) { *err = 0u; }
 
 // Rows of shard r, row t of a request with window base S - Q (w = S - Q + 1 + t).
 __device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W) {
@@ -95,7 +94,6 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  if (a.err_flag != nullptr) plan_clear_kernel<<<1, 1, 0, s>>>(a.err_flag);
   plan_kernel<<<(unsigned)a.N, kPlanThreads, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -137,6 +137,23 @@ def test_plan_device_error_bits():
     assert int(rows["err_flag"].item()) & mla.MLA_PLAN_ERR_ROWS
 
 
+def test_plan_error_flag_is_sticky():
+    """Bits are ORed in and never cleared by the library: a valid call leaves
+    an earlier error visible, and a zeroed flag stays zero over valid calls."""
+    bt = [[0, 1], [2, 3]]
+    t = lambda x: torch.tensor(x, dtype=torch.int32, device="cuda")
+    flag = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    args = lambda S: (t(S), t([0, 2, 5]), 5, 2, t(bt), 4, 16, 20)
+    mla.mla_verify_plan(*args([40, 30]), err_flag=flag)
+    mla.mla_verify_plan(*args([40, 30]), err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    mla.mla_verify_plan(*args([40, 2]), err_flag=flag)             # S < Q
+    mla.mla_verify_plan(*args([40, 30]), err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == mla.MLA_PLAN_ERR_QLEN
+
+
 def test_zero_query_pins_every_window():
     """q = 0: every score is 0, so the final lse is ln(window) and each shard's
     lse is ln(its row length) -- one token too many or too few on any shard
@@ -227,3 +244,35 @@ def test_named_workload_parity(name):
         f"excess={ex:.3f}")
     assert ex <= 1.0
     assert el <= TOL_LSE
+
+
+# ------------------------------------------------- merge shapes and paths ---
+
+MERGE_CASES = {
+    # more than 511 request boundaries: the merge's request search narrows in
+    # coarse rounds before its final one
+    "many_requests": dict(N=600, H=2, qlen_range=(1, 2), seq_range=(2, 40), block_size=16,
+                          W=2, kv_dtype="bf16", nseg=2),
+    # 2 x 70 = 140 segments per pair: statistics past the 128 held in registers
+    "segments_140": dict(N=2, H=2, qlen=3, seq_range=(2500, 3000), block_size=16, W=2,
+                         kv_dtype="bf16", nseg=70),
+    # 4 x 200 segments: too many for the LDS area, the sequential shard path
+    "segments_800": dict(N=2, H=2, qlen=2, seq_range=(3000, 3600), block_size=16, W=4,
+                         kv_dtype="bf16", nseg=200),
+}
+
+
+@pytest.mark.parametrize("name", list(MERGE_CASES))
+def test_merge_paths(name):
+    spec = MERGE_CASES[name]
+    inp = wl.make_workload(spec, seed=11)
+    say(f"merge case {name}: N={inp['N']} R={inp['R']} W={inp['W']} nseg={spec['nseg']}")
+    got = run_gpu(inp, want_shards=True)
+    ref = _check_plan(inp, got)
+    so, sl, _ = oracle_shard_results(inp, ref, spec["nseg"])
+    assert out_excess(got["shard_out"], so, "bf16") <= 1.0
+    assert max_err(got["shard_lse"], sl) <= TOL_LSE
+    out_ref, lse_ref = orc.verify_reference(inp)
+    say(f"  max|dout|={max_err(got['out'], out_ref):.3e} max|dlse|={max_err(got['lse'], lse_ref):.3e}")
+    assert out_excess(got["out"], out_ref, "bf16") <= 1.0
+    assert max_err(got["lse"], lse_ref) <= TOL_LSE

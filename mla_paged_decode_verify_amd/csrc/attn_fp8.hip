@@ -1,82 +1,121 @@
 // Split-K segmented MLA attention partials, fp8 (e4m3fn) KV cache.
 //
 // The quantities computed, the work decomposition and the per-tile
-// computation are those of attn_common.h. Specific to this kernel: the fp8
-// codes of the next tile are loaded into registers (lane l of wave w: chunks
-// 9w .. 9w+8 of token l) while the current tile is computed, and are widened
-// exactly to bf16 on the way into LDS; the scale is folded into the score
-// scale and the output.
+// computation are those of attn_common.h. Specific to this kernel:
+//  * The fp8 codes of a 64-token tile (36,864 B, token-major, 576 B per
+//    token) go straight from HBM to LDS with direct loads into a ring of two
+//    staging tiles; each wave loads the 16 tokens 16w .. 16w + 15 with nine
+//    1 KB instructions. While tile k is computed, tiles k+1 and k+2 are in
+//    flight.
+//  * Between two tiles the workgroup widens the next staged tile exactly to
+//    bf16 into the tile buffer the shared computation reads (every e4m3fn
+//    value is a bf16 value), in the latent / rope layout of attn_common.h.
+//  * The fp8 scale is folded into the score scale and into the output.
+// LDS: two staging tiles (73,728 B) + the bf16 tile buffer (75,776 B, which
+// first stages Q) + the exchange areas.
 #include "attn_common.h"
 
 namespace mla {
 namespace {
 
-// Widen 16 e4m3fn codes (one uint4) to 16 bf16 values (two uint4). Exact:
-// every e4m3fn value is a bf16 value.
-__device__ inline void fp8x16_to_bf16(uint4 in, uint4& lo, uint4& hi) {
-  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-  uint32_t o[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // v_cvt_pk_f32_fp8 reads the OCP e4m3fn format on gfx950.
-    auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-    auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-    // f32 -> bf16 by truncation is exact for these values.
-    o[2 * k] = (__float_as_uint(f01[0]) >> 16) | (__float_as_uint(f01[1]) & 0xFFFF0000u);
-    o[2 * k + 1] = (__float_as_uint(f23[0]) >> 16) | (__float_as_uint(f23[1]) & 0xFFFF0000u);
-  }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
+constexpr int kF8Tile = kTile * kHeadDim;    // 36,864 B of codes per tile
+constexpr int kF8Loads = kF8Tile / 1024 / 4; // 9 direct 1 KB loads per wave per tile
+static_assert(kF8Loads * 1024 == 16 * kHeadDim, "a wave's loads cover exactly 16 tokens");
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Widen 8 e4m3fn codes (a uint2) to 8 bf16 values (a uint4) with the gfx950
+// packed conversion at scale 1 -- exact: every e4m3fn value is a bf16 value.
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 in) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
-// fp8: lane l of wave w loads chunks [9w, 9w + 9) (16 codes each) of token l.
-struct Fp8Stage {
-  static constexpr int kLoads = kHeadDim / 16 / 4;  // 9
-  uint4 reg[kLoads];
-  int32_t sp;
-
-  __device__ inline void fetch_page(const AttnArgs& a, const int32_t* pt_row, int tb, int hi,
-                                    int lane) {
-    sp = subpage_always(a, pt_row, tb + lane, hi);
-  }
-  __device__ inline void load(const AttnArgs& a, const unsigned char* pool, int tb, int hi,
-                              int wave, int lane) {
-    const unsigned char* src =
-        token_src<kHeadDim>(a, pool, sp, tb + lane, hi, zero_row()) + 16 * kLoads * wave;
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) reg[j] = *reinterpret_cast<const uint4*>(src + 16 * j);
-  }
-  __device__ inline void store(unsigned char* dst, int wave, int lane) const {
-    const int row = lane;
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int col = kLoads * wave + j;      // 16-dim chunk
-      uint4 lo, hi4;
-      fp8x16_to_bf16(reg[j], lo, hi4);
-      if (col < kVDim / 16) {
-        *reinterpret_cast<uint4*>(dst + lat_off(row, 2 * col)) = lo;
-        *reinterpret_cast<uint4*>(dst + lat_off(row, 2 * col + 1)) = hi4;
-      } else {
-        const int c0 = 2 * (col - kVDim / 16);
-        unsigned char* rb = dst + kLatBytes + row * kRopeRow;
-        *reinterpret_cast<uint4*>(rb + 16 * (c0 ^ (row & 7))) = lo;
-        *reinterpret_cast<uint4*>(rb + 16 * ((c0 + 1) ^ (row & 7))) = hi4;
-      }
-    }
-  }
+// Sources of one wave's 16 tokens of a tile. Sub-pages of 16+ tokens: the
+// 16 tokens are contiguous in the pool (one base address, `nvalid` before the
+// segment end). Smaller sub-pages: one entry per token, looked up per load.
+struct F8Slice {
+  const unsigned char* base;
+  int nvalid;
 };
 
+// Load j (0..8) of this wave: staging bytes [9216 w + 1024 j, + 1024) of the
+// tile, i.e. byte o = 1024 j + 16 l of the wave's 16 tokens in lane l (a
+// lane's 16 bytes never straddle two tokens: 576 = 36 * 16).
+__device__ __forceinline__ void issue_f8_slice(const F8Slice& v, const unsigned char* zero,
+                                               unsigned char* stage, int wave, int lane, int j) {
+  const int o = 1024 * j + 16 * lane;
+  const int t = o / kHeadDim;
+  const unsigned char* src = t < v.nvalid ? v.base + o : zero + (o - t * kHeadDim);
+  dma16(src, stage + 16 * kHeadDim * wave + 1024 * j);
+}
+__device__ __forceinline__ void issue_f8_pages(const AttnArgs& a, const unsigned char* pool,
+                                               const int32_t* pt_row, int tb, int hi,
+                                               const unsigned char* zero, unsigned char* stage,
+                                               int wave, int lane, int j) {
+  const int o = 1024 * j + 16 * lane;
+  const int t = o / kHeadDim;
+  const int tok = tb + 16 * wave + t;
+  const int32_t sp = subpage_always(a, pt_row, tok, hi);
+  const unsigned char* src = token_src<kHeadDim>(a, pool, sp, tok, hi, zero);
+  dma16(src + (o - t * kHeadDim), stage + 16 * kHeadDim * wave + 1024 * j);
+}
+
+// Sub-pages of 64 consecutive tiles for one wave: lane j holds the sub-page
+// of tokens tb0 + 64 j + 16 w .. +15 (clamped to the last in-range token).
+__device__ __forceinline__ int32_t f8_slice_pages(const AttnArgs& a, const int32_t* pt_row,
+                                                  int tb0, int hi, int wave, int lane) {
+  const int64_t tok = min((int64_t)tb0 + (int64_t)kTile * lane + 16 * wave, (int64_t)hi - 1);
+  return pt_row[tok >> a.page_shift];
+}
+
+// Widen a staged tile into the bf16 tile buffer, 8 codes (one 16-byte bf16
+// chunk h: dims 8h .. 8h + 7) per lane and pass. The 16 lanes of group G
+// (G = tid / 16) take tokens 8 (G % 8) + 0..7 and the chunk pair
+// 2b, 2b + 1 with b = 2i + G / 8 in pass i (i = 0..17): their 16-byte
+// writes then fall on 16 distinct 4-bank groups of the latent rows (row
+// stride 264 dwords) and of the swizzled rope rows, so no store conflicts;
+// the 8-byte reads of the staged codes conflict at most two ways.
+__device__ __forceinline__ void widen_tile(const unsigned char* stage, unsigned char* buf,
+                                           int tid) {
+  const int G = tid >> 4;
+  const int tok = 8 * (G & 7) + (tid & 7);
+  const int bit = (tid >> 3) & 1;
+  const unsigned char* src = stage + tok * kHeadDim + 8 * bit;
+  unsigned char* lat = buf + tok * kLatRow;
+  unsigned char* rope = buf + kLatBytes + tok * kRopeRow;
+#pragma unroll
+  for (int i0 = 0; i0 < 18; i0 += 6) {
+    uint2 in[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int h0 = 2 * (2 * (i0 + i) + (G >> 3));   // even chunk of the pair
+      in[i] = *reinterpret_cast<const uint2*>(src + 8 * h0);
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int h = 2 * (2 * (i0 + i) + (G >> 3)) + bit;
+      const uint4 w = fp8x8_to_bf16(in[i]);
+      if (h < kVDim / 8)
+        *reinterpret_cast<uint4*>(lat + 16 * (h ^ lat_swz(tok))) = w;
+      else
+        *reinterpret_cast<uint4*>(rope + 16 * ((h - kVDim / 8) ^ (tok & 7))) = w;
+    }
+  }
+}
+
+template <bool SLICE>
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
-  // Two separate arrays (not one indexed one), so that the compiler can tell
-  // the buffer being read from the buffer being filled.
-  __shared__ __align__(16) unsigned char buf0[kBufBytes];
-  __shared__ __align__(16) unsigned char buf1[kBufBytes];
+  __shared__ __align__(16) unsigned char stage[2 * kF8Tile];  // staging tiles 0, 1
+  __shared__ __align__(16) unsigned char buf[kBufBytes];
   __shared__ PExchange px;
   __shared__ RowExchange rx;
-  const WorkUnit u = decode_unit(a, blockIdx.x);
+  WorkUnit u = decode_head(a, blockIdx.x);
   if (!u.valid) return;
-  const int lo = u.lo, hi = u.hi;
-  if (lo >= hi) return;                     // segment inactive for the whole group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,16 +125,44 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   const int r16 = lane & 15;
 
   const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kHeadDim;
+  const unsigned char* zero = zero_row();
   const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
 
-  // ---- first tile in flight before anything else
-  Fp8Stage fs;
-  fs.fetch_page(a, pt_row, lo, hi, lane);
-  fs.load(a, pool, lo, hi, wave, lane);
-  fs.fetch_page(a, pt_row, lo + kTile, hi, lane);
+  // ---- Q first (it needs only the request's rows), staged in the tile buffer
+  issue_q_tile(a, u, buf, wave, lane, zero);
+  decode_tail(a, u);
+  const int lo = u.lo, hi = u.hi;
+  if (lo >= hi) {                           // segment inactive for the whole group:
+    MLA_WAIT_VMCNT(0);                      // let the Q loads land before the LDS is released
+    return;
+  }
+  const int ntiles = (hi - lo + kTile - 1) / kTile;
 
-  // ---- Q through the second tile buffer (first written at the second step)
-  issue_q_tile(a, u, buf1, wave, lane, zero_row());
+  int32_t vpg = 0;                          // SLICE: sub-pages of tiles 64q .. 64q + 63
+  auto issue_tile = [&](int t) {
+    unsigned char* st = stage + (t & 1) * kF8Tile;
+    const int tb = lo + t * kTile;
+    if constexpr (SLICE) {
+      if ((t & 63) == 0) vpg = f8_slice_pages(a, pt_row, tb, hi, wave, lane);
+      const int32_t sp = __builtin_amdgcn_readlane(vpg, t & 63);
+      F8Slice v;
+      const bool ok = sp >= 0 && sp < a.num_subpages;
+      const int t0 = tb + 16 * wave;
+      v.nvalid = ok ? min(max(hi - t0, 0), 16) : 0;
+      v.base = pool + (((int64_t)(ok ? sp : 0) << a.page_shift) + (t0 & (a.page_size - 1))) *
+                          kHeadDim;
+#pragma unroll
+      for (int j = 0; j < kF8Loads; ++j) issue_f8_slice(v, zero, st, wave, lane, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kF8Loads; ++j)
+        issue_f8_pages(a, pool, pt_row, tb, hi, zero, st, wave, lane, j);
+    }
+  };
+
+  // ---- tiles 0 and 1 in flight with Q; Q into registers; tile 0 widened
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
   int mrow[2], hi_row[2];
   bool row_ok[2];
   lane_rows(a, u, g, r16, mrow, hi_row, row_ok);
@@ -104,32 +171,38 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   MLA_WAIT_VMCNT(0);
   lds_barrier();
   bf16x8 qf[2][kQSteps];
-  read_q(buf1, g, lane, qf);
+  read_q(buf, g, lane, qf);
+  lds_barrier();                            // every wave holds its Q: the buffer is free
+  widen_tile(stage, buf, tid);
+  lds_barrier();                            // tile 0 in the buffer; staging tile 0 is free
+  if (ntiles > 2) issue_tile(2);
 
-  // One tile: widen the staged codes into `cur`, start loading the next tile's
-  // codes, then compute on `cur` (last read two tiles ago, before the previous
-  // barrier).
-  auto step = [&](unsigned char* cur, int tb) {
-    fs.store(cur, wave, lane);
-    lds_barrier();
-    if (tb + kTile < hi) {
-      fs.load(a, pool, tb + kTile, hi, wave, lane);
-      fs.fetch_page(a, pt_row, tb + 2 * kTile, hi, lane);
+  for (int k = 0; k < ntiles; ++k) {
+    compute_tile(buf, &px, qf, st, lo + k * kTile, hi_row, a.qk_scale_log2, g, c, lane,
+                 [](int) {}, [] {});
+    if (k + 1 < ntiles) {
+      // tile k + 1 has landed (this wave's later loads: tile k + 2's nine)
+      if (k + 2 < ntiles) MLA_WAIT_VMCNT(kF8Loads); else MLA_WAIT_VMCNT(0);
+      lds_barrier();                        // ... for every wave; the buffer is no longer read
+      widen_tile(stage + ((k + 1) & 1) * kF8Tile, buf, tid);
+      lds_barrier();                        // tile k + 1 in the buffer; its staging tile is free
+      if (k + 3 < ntiles) issue_tile(k + 3);
     }
-    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, [](int) {}, [] {});
-  };
-  for (int tb = lo; tb < hi; tb += 2 * kTile) {
-    step(buf0, tb);
-    if (tb + kTile >= hi) break;
-    step(buf1, tb + kTile);
   }
-  store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);
+
+  // row group 0 stages its O in the tile buffer, row group 1 in the staging tiles
+  store_partials(a, u, st, rx, g == 0 ? buf : stage, mrow, row_ok, g, c, lane);
 }
+
+static_assert(2 * kF8Tile >= 32 * kStageRow, "a row group's O fits the two staging tiles");
 
 }  // namespace
 
 hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s) {
-  attn_fp8_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  if (a.page_size >= 16)
+    attn_fp8_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  else
+    attn_fp8_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,11 @@ SMALL = {
     "verify_w8_b48_p16": small_spec(W=8, block_size=48, seq_range=(100, 1000), qlen=5),
     "odd_block_p1": small_spec(W=2, block_size=3, seq_range=(20, 90), qlen=2, H=4),
     "fp8_w4": small_spec(W=4, kv_dtype="fp8_e4m3", qlen=7, H=12, seq_range=(100, 600)),
+    # fp8 with 4-token sub-pages (per-token page lookups) and with 16-token ones
+    "fp8_odd_block_p4": small_spec(W=3, block_size=12, kv_dtype="fp8_e4m3", qlen=3, H=8,
+                                   seq_range=(40, 500)),
+    "fp8_b48_p16": small_spec(W=2, block_size=48, kv_dtype="fp8_e4m3", qlen=5, H=12,
+                              seq_range=(150, 900)),
     "heads128_q8": small_spec(N=2, H=128, qlen=8, W=1, block_size=256, seq_range=(100, 300)),
     "heads12_q7_m84": small_spec(N=3, H=12, qlen=7, W=2, seq_range=(70, 260)),
     "ragged_q": dict(N=5, H=8, qlen_range=(1, 8), seq_range=(8, 200), block_size=32, W=3,

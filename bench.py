@@ -229,6 +229,47 @@ def main():
     a1.record()
     torch.cuda.synchronize()
     attn_launch_ms = a0.elapsed_time(a1) / n_attn
+
+    # Attention + merge (the hot path without the once-per-forward plan), per
+    # eager step from the step events: median and min.
+    am = np.array([e[1].elapsed_time(e[3]) for e in ev]) * 1e3
+
+    # One GPU's share in a real DCP deployment: shard 0 alone at its real
+    # shape (its pool, its row lengths and page table), back to back.
+    shard_us = None
+    if W > 1:
+        kv0 = [kv[0:1] for kv in kvs]
+        p0 = (torch.empty((1, R, H, nseg, 512), **f32), torch.empty((1, R, H, nseg), **f32),
+              torch.empty((1, R, H, nseg), **f32))
+        rl0, pt0 = plan_bufs["row_lens"][0:1], plan_bufs["page_table"][0:1]
+        attn0 = lambda k: mla.mla_verify_attn(
+            dev["q"], kv0[k % len(kv0)], rl0, pt0, dev["q_start"], page_size=page_size,
+            max_qlen=dev["max_qlen"], nseg=nseg, sm_scale=dev["sm_scale"],
+            kv_scale=dev["kv_scale"], segm_out=p0[0], segm_max=p0[1], segm_expsum=p0[2])
+        for k in range(3):
+            attn0(k)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for k in range(n_attn):
+            attn0(k)
+        s1.record()
+        torch.cuda.synchronize()
+        shard_us = s0.elapsed_time(s1) / n_attn * 1e3
+        del p0
+
+    # Measured copy peak: a 2 GiB elementwise copy (read + write), larger than
+    # the Infinity Cache, timed with events.
+    cp = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    cq = torch.empty_like(cp)
+    torch.mul(cp, 1.0, out=cq)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        torch.mul(cp, 1.0, out=cq)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * cp.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cp, cq
     ms_step = wall * 1e3 / args.steps
     achieved = kv_bytes / (attn_launch_ms * 1e-3) / 1e9
     res = {
@@ -251,11 +292,19 @@ def main():
         "eager_split_us": {"plan": round(plan_ms * 1e3, 2), "attn": round(attn_ms * 1e3, 2),
                       "merge": round(merge_ms * 1e3, 2),
                       "attn_back_to_back": round(attn_launch_ms * 1e3, 2)},
+        "attn_merge_us": {"median": round(float(np.median(am)), 2), "min": round(float(am.min()), 2),
+                          "kv_gbs_median": round(kv_bytes / (float(np.median(am)) * 1e-6) / 1e9, 1)},
+        "shard0_alone_attn_us": None if shard_us is None else round(shard_us, 2),
+        "bytes": {"kv_algorithmic": kv_bytes, "q": R * H * 1152, "out": R * H * (1024 + 4),
+                  "partials": W * R * H * nseg * (2048 + 8)},
+        "t_roof_us": round(max(kv_bytes / (HBM_PEAK_GBS * 1e9), flops / 2.5e15) * 1e6, 2),
+        "hbm_copy_peak_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(args.workload),
                      "kernel": "attn_bf16_kernel" if inp["kv_dtype"] == "bf16" else "attn_fp8_kernel",
-                     "bytes_per_launch": kv_bytes, "flops_per_launch": flops},
+                     "bytes_per_launch": kv_bytes, "flops_per_launch": flops,
+                     "frac_of_copy_peak": round(achieved / copy_gbs, 4)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -279,7 +279,8 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if inp["kv_dtype"] == "bf16" else "fp8e4m3-kv/bf16",
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8e4m3-kv/bf16",
+                  "fp8_e5m2": "fp8e5m2-kv/bf16"}[inp["kv_dtype"]],
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp["N"], "heads": H,
                    "qlen": int(np.max(inp["qlens"])), "rows": R, "shards": W,

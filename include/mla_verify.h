@@ -49,8 +49,11 @@ typedef enum {
 
 typedef enum {
   MLA_KV_BF16 = 0,     /* bf16 cache entries, 1152 bytes per token           */
-  MLA_KV_FP8_E4M3 = 1  /* OCP e4m3fn codes, 576 bytes per token, real value =
+  MLA_KV_FP8_E4M3 = 1, /* OCP e4m3fn codes, 576 bytes per token, real value =
                           code * kv_scale (one per-tensor float scale)       */
+  MLA_KV_FP8_E5M2 = 2  /* OCP e5m2 codes (the fp8_e5m2 cache dtype of the
+                          [V51011] fp8 routing test grid), 576 bytes per
+                          token, real value = code * kv_scale               */
 } mla_kv_dtype_t;
 
 #define MLA_HEAD_DIM 576
@@ -135,7 +138,7 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
  *
  *   q          [R, H, 576] bf16 queries (RoPE already applied)
  *   kv         [W, num_blocks, block_size, 576] cache: one pool per shard,
- *              elements bf16 or e4m3fn per kv_dtype; 16-byte aligned
+ *              elements bf16, e4m3fn or e5m2 per kv_dtype; 16-byte aligned
  *   kv_scale   fp8 descale (real = code * kv_scale), > 0; ignored for bf16
  *   sm_scale   softmax scale applied to <q, k> (e.g. 1/sqrt(576)), > 0; the
  *              product sm_scale * kv_scale * log2(e) must be a positive

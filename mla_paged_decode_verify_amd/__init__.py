@@ -13,7 +13,8 @@ import torch
 
 from . import _lib
 from ._lib import (MLA_ERR_HIP, MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED,  # noqa: F401
-                   MLA_KV_BF16, MLA_KV_FP8_E4M3, MLA_OK, MLA_PLAN_ERR_BLOCKS,
+                   MLA_KV_BF16, MLA_KV_FP8_E4M3, MLA_KV_FP8_E5M2, MLA_OK,
+                   MLA_PLAN_ERR_BLOCKS,
                    MLA_PLAN_ERR_BOUND, MLA_PLAN_ERR_QLEN, MLA_PLAN_ERR_ROWS)
 
 HEAD_DIM = 576
@@ -118,14 +119,17 @@ def _kv_dtype(kv):
         return MLA_KV_BF16
     if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
         return MLA_KV_FP8_E4M3
-    raise TypeError(f"kv must be bfloat16 or e4m3fn (uint8) codes, got {kv.dtype}")
+    if kv.dtype == torch.float8_e5m2:
+        return MLA_KV_FP8_E5M2
+    raise TypeError(f"kv must be bfloat16, e4m3fn (uint8) or e5m2 codes, got {kv.dtype}")
 
 
 def mla_verify_attn(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen,
                     nseg, sm_scale, kv_scale=1.0, segm_out=None, segm_max=None,
                     segm_expsum=None, stream=None):
     """Split-K partials. q [R, H, 576] bf16; kv [W, num_blocks, block_size, 576]
-    bf16 or e4m3fn codes. Returns (segm_out, segm_max, segm_expsum)."""
+    bf16, e4m3fn codes (uint8 or float8_e4m3fn) or e5m2 codes (float8_e5m2).
+    Returns (segm_out, segm_max, segm_expsum)."""
     _dev(q, torch.bfloat16, "q")
     _dev(kv, None, "kv")
     kvd = _kv_dtype(kv)

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_verify.so")
 
 MLA_OK, MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
-MLA_KV_BF16, MLA_KV_FP8_E4M3 = 0, 1
+MLA_KV_BF16, MLA_KV_FP8_E4M3, MLA_KV_FP8_E5M2 = 0, 1, 2
 MLA_PLAN_ERR_QLEN, MLA_PLAN_ERR_BOUND, MLA_PLAN_ERR_BLOCKS, MLA_PLAN_ERR_ROWS = 1, 2, 4, 8
 
 EXPORTED = {

@@ -134,9 +134,9 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
                 page_size, block_size);
   if (num_blocks < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: num_blocks must be >= 1");
   if (pt_width < 0) return fail(MLA_ERR_INVALID, "mla_verify_attn: pt_width must be >= 0");
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_FP8_E5M2)
     return fail(MLA_ERR_UNSUPPORTED, "mla_verify_attn: unknown kv_dtype %d", (int)kv_dtype);
-  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  const bool fp8 = kv_dtype != MLA_KV_BF16;
   const double log2e = 1.4426950408889634;
   const float qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)kv_scale : 1.0) * log2e);
   // the kernels take the row maximum of unscaled scores, which needs a
@@ -166,6 +166,7 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
   a.mblocks = (int32_t)mblocks;
   a.qk_scale_log2 = qk_scale_log2;
   a.v_scale = fp8 ? kv_scale : 1.0f;
+  a.e5m2 = kv_dtype == MLA_KV_FP8_E5M2 ? 1 : 0;
   a.segm_out = segm_out; a.segm_max = segm_max; a.segm_expsum = segm_expsum;
   return hip_status(mla::launch_attn(a, fp8, (hipStream_t)stream), "mla_verify_attn launch");
 }

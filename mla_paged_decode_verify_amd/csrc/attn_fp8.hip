@@ -1,4 +1,5 @@
-// Split-K segmented MLA attention partials, fp8 (e4m3fn) KV cache.
+// Split-K segmented MLA attention partials, fp8 KV cache (OCP e4m3fn or e5m2
+// codes).
 //
 // The quantities computed, the work decomposition and the per-tile
 // computation are those of attn_common.h. Specific to this kernel:
@@ -8,8 +9,9 @@
 //    1 KB instructions. While tile k is computed, tiles k+1 and k+2 are in
 //    flight.
 //  * Between two tiles the workgroup widens the next staged tile exactly to
-//    bf16 into the tile buffer the shared computation reads (every e4m3fn
-//    value is a bf16 value), in the latent / rope layout of attn_common.h.
+//    bf16 into the tile buffer the shared computation reads (every e4m3fn and
+//    every e5m2 value is a bf16 value), in the latent / rope layout of
+//    attn_common.h.
 //  * The fp8 scale is folded into the score scale and into the output.
 // LDS: two staging tiles (73,728 B) + the bf16 tile buffer (75,776 B, which
 // first stages Q) + the exchange areas.
@@ -24,15 +26,26 @@ static_assert(kF8Loads * 1024 == 16 * kHeadDim, "a wave's loads cover exactly 16
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Widen 8 e4m3fn codes (a uint2) to 8 bf16 values (a uint4) with the gfx950
-// packed conversion at scale 1 -- exact: every e4m3fn value is a bf16 value.
+// Widen 2 codes (the low or high half of a word) to 2 bf16 values with the
+// gfx950 packed conversion at scale 1: e4m3fn ("fp8") or e5m2 ("bf8").
+template <bool E5M2>
+__device__ __forceinline__ uint32_t cvt2(uint32_t w, bool hi) {
+  bf16x2_t r;
+  if constexpr (E5M2) {
+    r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+  } else {
+    r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+// 8 codes (a uint2) to 8 bf16 values (a uint4). Exact: every e4m3fn and every
+// e5m2 value is a bf16 value (bf16 has more exponent and mantissa bits).
+template <bool E5M2>
 __device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 in) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.x, 1.0f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.x, 1.0f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.y, 1.0f, false);
-  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.y, 1.0f, true);
-  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+  return make_uint4(cvt2<E5M2>(in.x, false), cvt2<E5M2>(in.x, true), cvt2<E5M2>(in.y, false),
+                    cvt2<E5M2>(in.y, true));
 }
 
 // Sources of one wave's 16 tokens of a tile. Sub-pages of 16+ tokens: the
@@ -80,6 +93,7 @@ __device__ __forceinline__ int32_t f8_slice_pages(const AttnArgs& a, const int32
 // writes then fall on 16 distinct 4-bank groups of the latent rows (row
 // stride 264 dwords) and of the swizzled rope rows, so no store conflicts;
 // the 8-byte reads of the staged codes conflict at most two ways.
+template <bool E5M2>
 __device__ __forceinline__ void widen_tile(const unsigned char* stage, unsigned char* buf,
                                            int tid) {
   const int G = tid >> 4;
@@ -99,7 +113,7 @@ __device__ __forceinline__ void widen_tile(const unsigned char* stage, unsigned 
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
       const int h = 2 * (2 * (i0 + i) + (G >> 3)) + bit;
-      const uint4 w = fp8x8_to_bf16(in[i]);
+      const uint4 w = fp8x8_to_bf16<E5M2>(in[i]);
       if (h < kVDim / 8)
         *reinterpret_cast<uint4*>(lat + 16 * (h ^ lat_swz(tok))) = w;
       else
@@ -108,7 +122,7 @@ __device__ __forceinline__ void widen_tile(const unsigned char* stage, unsigned 
   }
 }
 
-template <bool SLICE>
+template <bool SLICE, bool E5M2>
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   __shared__ __align__(16) unsigned char stage[2 * kF8Tile];  // staging tiles 0, 1
   __shared__ __align__(16) unsigned char buf[kBufBytes];
@@ -173,7 +187,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   bf16x8 qf[2][kQSteps];
   read_q(buf, g, lane, qf);
   lds_barrier();                            // every wave holds its Q: the buffer is free
-  widen_tile(stage, buf, tid);
+  widen_tile<E5M2>(stage, buf, tid);
   lds_barrier();                            // tile 0 in the buffer; staging tile 0 is free
   if (ntiles > 2) issue_tile(2);
 
@@ -184,7 +198,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
       // tile k + 1 has landed (this wave's later loads: tile k + 2's nine)
       if (k + 2 < ntiles) MLA_WAIT_VMCNT(kF8Loads); else MLA_WAIT_VMCNT(0);
       lds_barrier();                        // ... for every wave; the buffer is no longer read
-      widen_tile(stage + ((k + 1) & 1) * kF8Tile, buf, tid);
+      widen_tile<E5M2>(stage + ((k + 1) & 1) * kF8Tile, buf, tid);
       lds_barrier();                        // tile k + 1 in the buffer; its staging tile is free
       if (k + 3 < ntiles) issue_tile(k + 3);
     }
@@ -199,10 +213,14 @@ static_assert(2 * kF8Tile >= 32 * kStageRow, "a row group's O fits the two stagi
 }  // namespace
 
 hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s) {
-  if (a.page_size >= 16)
-    attn_fp8_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(a);
-  else
-    attn_fp8_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  const bool slice = a.page_size >= 16;
+  if (a.e5m2) {
+    if (slice) attn_fp8_kernel<true, true><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+    else attn_fp8_kernel<false, true><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  } else {
+    if (slice) attn_fp8_kernel<true, false><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+    else attn_fp8_kernel<false, false><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct AttnArgs {
   int32_t mblocks;           // ceil(max_qlen * H / rows per workgroup)
   float qk_scale_log2;       // sm_scale * (fp8: kv_scale) * log2(e)
   float v_scale;             // fp8: kv_scale, bf16: 1
+  int32_t e5m2;              // fp8 codes: 0 e4m3fn, 1 e5m2
   float* segm_out;
   float* segm_max;
   float* segm_expsum;

@@ -37,6 +37,7 @@ __all__ = [
     "HEAD_DIM", "V_DIM", "LN2", "LOG2E",
     "subpage_size", "window_length", "row_view", "qo_indptr", "subpage_table",
     "plan", "decode_bf16", "e4m3fn_value", "e4m3fn_table", "decode_e4m3fn",
+    "e5m2_value", "e5m2_table", "decode_e5m2",
     "gather_request_kv", "attention_rows", "shard_local_kv",
     "shard_attention_rows", "segment_partials", "segment_merge", "lse_merge",
     "two_stage_verify", "verify_reference", "request_rows",
@@ -203,6 +204,37 @@ def decode_e4m3fn(codes) -> np.ndarray:
     return _E4M3_TABLE[np.asarray(codes).astype(np.int64)]
 
 
+def e5m2_value(byte: int) -> float:
+    """Value of one OCP FP8 E5M2 byte.
+
+    [V51011] the new fp8 routing test lists fp8_e5m2 beside fp8_e4m3 as a KV
+    cache dtype; the format is taken from its published definition: 1 sign
+    bit, 5 exponent bits with bias 15, 2 mantissa bits; exponent 0 is
+    subnormal (m/4 * 2^-14); exponent 31 is infinity (m = 0) or NaN, so the
+    largest finite value is 1.75 * 2^15 = 57344.
+    """
+    byte = int(byte) & 0xFF
+    sign = -1.0 if byte & 0x80 else 1.0
+    exp = (byte >> 2) & 0x1F
+    man = byte & 0x3
+    if exp == 0x1F:
+        return sign * float("inf") if man == 0 else float("nan")
+    if exp == 0:
+        return sign * (man / 4.0) * 2.0 ** (1 - 15)
+    return sign * (1.0 + man / 4.0) * 2.0 ** (exp - 15)
+
+
+def e5m2_table() -> np.ndarray:
+    return np.array([e5m2_value(b) for b in range(256)], dtype=np.float64)
+
+
+_E5M2_TABLE = e5m2_table()
+
+
+def decode_e5m2(codes) -> np.ndarray:
+    return _E5M2_TABLE[np.asarray(codes).astype(np.int64)]
+
+
 # --------------------------------------------------------------------------
 # Reading a request's logical KV back out of the sharded paged cache
 # --------------------------------------------------------------------------
@@ -227,6 +259,8 @@ def gather_request_kv(cache, kv_dtype: str, kv_scale: float, block_table_row,
         return decode_bf16(raw)
     if kv_dtype == "fp8_e4m3":
         return decode_e4m3fn(raw) * float(kv_scale)
+    if kv_dtype == "fp8_e5m2":
+        return decode_e5m2(raw) * float(kv_scale)
     raise ValueError(kv_dtype)
 
 

@@ -50,6 +50,10 @@ SMALL = {
                                    seq_range=(40, 500)),
     "fp8_b48_p16": small_spec(W=2, block_size=48, kv_dtype="fp8_e4m3", qlen=5, H=12,
                               seq_range=(150, 900)),
+    # e5m2 codes (the fp8_e5m2 cache dtype), 64- and 4-token sub-pages
+    "e5m2_w4": small_spec(W=4, kv_dtype="fp8_e5m2", qlen=7, H=12, seq_range=(100, 600)),
+    "e5m2_odd_block_p4": small_spec(W=3, block_size=12, kv_dtype="fp8_e5m2", qlen=2, H=8,
+                                    seq_range=(40, 400)),
     "heads128_q8": small_spec(N=2, H=128, qlen=8, W=1, block_size=256, seq_range=(100, 300)),
     "heads12_q7_m84": small_spec(N=3, H=12, qlen=7, W=2, seq_range=(70, 260)),
     "ragged_q": dict(N=5, H=8, qlen_range=(1, 8), seq_range=(8, 200), block_size=32, W=3,
@@ -204,19 +208,22 @@ def test_output_discriminates_off_by_one_window():
     assert checked >= 6
 
 
-def test_fp8_every_finite_code_decodes():
-    """Fill every used cache slot with codes cycling through all 254 finite
-    e4m3fn values; the oracle decodes them from the bit definition."""
-    spec = small_spec(N=2, W=2, kv_dtype="fp8_e4m3", qlen=3, H=4, seq_range=(200, 300))
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "fp8_e5m2"])
+def test_fp8_every_finite_code_decodes(fmt):
+    """Fill every used cache slot with codes cycling through all finite values
+    of the format (254 e4m3fn codes, 248 e5m2 codes); the oracle decodes them
+    from the bit definition."""
+    spec = small_spec(N=2, W=2, kv_dtype=fmt, qlen=3, H=4, seq_range=(200, 300))
     inp = wl.make_workload(spec, seed=6)
-    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    table = orc.e4m3fn_table() if fmt == "fp8_e4m3" else orc.e5m2_table()
+    finite = np.array([c for c in range(256) if np.isfinite(table[c])], dtype=np.uint8)
     cache = inp["kv_bits"]
-    used = cache != wl.E4M3_NAN
+    used = cache != wl.E4M3_NAN                       # 0x7F is the canary of both formats
     cache[used] = np.resize(finite, int(used.sum()))
-    inp["kv_scale"] = 1.0 / 448.0
+    inp["kv_scale"] = 1.0 / float(np.max(np.abs(table[finite])))
     got = run_gpu(inp)
     out_ref, lse_ref = orc.verify_reference(inp)
-    assert out_excess(got["out"], out_ref, "fp8_e4m3") <= 1.0
+    assert out_excess(got["out"], out_ref, fmt) <= 1.0
     assert max_err(got["lse"], lse_ref) <= TOL_LSE
 
 

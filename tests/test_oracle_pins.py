@@ -138,7 +138,8 @@ def _logical_f64(inp, i):
     if inp["kv_dtype"] == "bf16":
         t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
         return t.to(torch.float64).numpy()
-    t = torch.from_numpy(bits).view(torch.float8_e4m3fn)
+    fmt = torch.float8_e4m3fn if inp["kv_dtype"] == "fp8_e4m3" else torch.float8_e5m2
+    t = torch.from_numpy(bits).view(fmt)
     return t.to(torch.float64).numpy() * inp["kv_scale"]
 
 
@@ -194,6 +195,20 @@ def test_e4m3fn_table_matches_torch_cast_and_known_values():
     assert np.sum(np.isnan(ours)) == 2 and not np.any(np.isinf(ours))
 
 
+def test_e5m2_table_matches_torch_cast_and_known_values():
+    ours = orc.e5m2_table()
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    ok = ~np.isnan(ours)
+    assert np.array_equal(ours[ok], lib[ok])
+    assert ours[0x7B] == 57344.0 and ours[0xFB] == -57344.0
+    assert ours[0x01] == 2.0 ** -16 and ours[0x04] == 2.0 ** -14
+    assert ours[0x3C] == 1.0 and ours[0x00] == 0.0
+    assert ours[0x7C] == np.inf and ours[0xFC] == -np.inf
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFD])
+    assert np.sum(np.isnan(ours)) == 6 and np.sum(np.isinf(ours)) == 2
+
+
 def test_bf16_decode_matches_torch():
     bits = np.random.default_rng(0).integers(0, 65536, 4096, dtype=np.uint32).astype(np.uint16)
     lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
@@ -203,7 +218,7 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(ours[ok], lib[ok])
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3", "fp8_e5m2"])
 def test_gather_matches_generator_logical_kv(kv):
     inp = _small_workload(seed=3, W=4, B=16, kv=kv)
     for i in range(inp["N"]):

@@ -32,6 +32,7 @@ import torch
 HEAD_DIM = 576
 BF16_NAN = 0x7FC0
 E4M3_NAN = 0x7F
+E5M2_NAN = 0x7F
 
 CONFIGS = {
     # batch 2, 16 heads, qlen 1, seq_len {37, 64}, block 16, 1 shard
@@ -141,6 +142,15 @@ def make_workload(spec, seed: int = 0, *, q_mode: str = "normal",
                  .view(torch.uint8).numpy() for k in ks]
         del ks
         per_req = (lambda i: codes[i])
+    elif kv_dtype == "fp8_e5m2":
+        cache = np.full((W, num_blocks, B, HEAD_DIM), E5M2_NAN, dtype=np.uint8)
+        ks = [draw(i) for i in range(N)]
+        amax = max(float(k.abs().max()) for k in ks)
+        kv_scale = amax / 57344.0
+        codes = [(k / kv_scale).clamp(-57344.0, 57344.0).to(torch.float8_e5m2)
+                 .view(torch.uint8).numpy() for k in ks]
+        del ks
+        per_req = (lambda i: codes[i])
     else:
         raise ValueError(kv_dtype)
 
@@ -190,6 +200,8 @@ def to_device(inp, device="cuda"):
     q = _t.from_numpy(inp["q_bits"].view(np.int16)).view(_t.bfloat16).to(device)
     if inp["kv_dtype"] == "bf16":
         kv = _t.from_numpy(inp["kv_bits"].view(np.int16)).view(_t.bfloat16).to(device)
+    elif inp["kv_dtype"] == "fp8_e5m2":
+        kv = _t.from_numpy(inp["kv_bits"]).view(_t.float8_e5m2).to(device)
     else:
         kv = _t.from_numpy(inp["kv_bits"]).to(device)
     i32 = lambda a: _t.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)

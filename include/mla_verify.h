@@ -13,8 +13,10 @@
  * Notation. N requests; request i has S_i cached tokens (its Q_i verify tokens
  * included, all already written to the cache) and Q_i >= 1 verify rows. Rows
  * are request-major: row rho = q_start[i] + t, t in [0, Q_i), R = q_start[N].
- * W shards hold each sequence round-robin with interleave 1: global position p
- * lives on shard p % W at local index p / W. H heads. Head dim 576 = 512
+ * W shards hold each sequence round-robin with interleave I (default 1): runs
+ * of I consecutive positions are dealt to shards 0, 1, ..., W-1 in turn, so
+ * global position p lives on shard (p / I) % W at local index
+ * (p / (I W)) I + p % I (for I = 1: shard p % W, local index p / W). H heads. Head dim 576 = 512
  * latent + 64 rope; V is the 512 latent values of the same cache entry.
  *
  * Conventions for every call below.
@@ -43,7 +45,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID = 1,     /* bad argument; nothing was launched            */
-  MLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. interleave>1) */
+  MLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. unknown kv dtype) */
   MLA_ERR_HIP = 3          /* a HIP launch failed                           */
 } mla_status_t;
 
@@ -63,7 +65,9 @@ typedef enum {
  * any of these problems gets row length 0 on every shard and an all -1
  * sub-page table, so later calls never read outside the caller's buffers. */
 #define MLA_PLAN_ERR_QLEN 1u    /* Q_i < 1, S_i < Q_i, or q_start not monotone  */
-#define MLA_PLAN_ERR_BOUND 2u   /* ceil(S_i / W) > max_kv_seq_len               */
+#define MLA_PLAN_ERR_BOUND 2u   /* longest local sequence of request i (shard
+                                   0's; ceil(S_i / W) for interleave 1) >
+                                   max_kv_seq_len                              */
 #define MLA_PLAN_ERR_BLOCKS 4u  /* request needs more than max_blocks blocks, or
                                    a block id it uses is outside [0,num_blocks) */
 #define MLA_PLAN_ERR_ROWS 8u    /* q_start[N] != R                              */
@@ -99,9 +103,14 @@ size_t mla_verify_workspace_bytes(int32_t W, int32_t R, int32_t H, int32_t nseg)
  *
  *   seq_lens    [N]   int32  S_i
  *   q_start     [N+1] int32  row offsets (q_start[0] = 0, q_start[N] = R)
- *   interleave  must be 1 (round-robin one token at a time); any other value
- *               returns MLA_ERR_UNSUPPORTED ([V51705] item 1: only
- *               interleave 1 has a verified per-row window)
+ *   interleave  I >= 1, with I * W <= 2^30 (else MLA_ERR_INVALID). The
+ *               pages' routing accepts only I = 1 ([V51705]: the per-row
+ *               window is verified only for interleave 1); I > 1 follows the
+ *               placement above, under which every row's window is still a
+ *               prefix of each shard's local sequence: shard r holds
+ *               c I + clamp(rem - r I, 0, I) positions of a window of w, with
+ *               c = w / (I W), rem = w % (I W). The bound check uses the
+ *               longest local sequence, shard 0's.
  *   block_table [N, max_blocks] int32 physical block ids, one table shared by
  *               every shard's pool; local token j of request i is in block
  *               block_table[i][j / block_size] at offset j % block_size

@@ -213,7 +213,8 @@ def mla_verify_forward(dev, *, nseg=1, plan=None, partials=None, out=None, lse=N
     if plan is None:
         plan = mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
                                dev["block_table"], dev["num_blocks"], dev["block_size"],
-                               dev["max_kv_seq_len"], stream=stream)
+                               dev["max_kv_seq_len"], interleave=dev.get("interleave", 1),
+                               stream=stream)
     kw = {}
     if partials is not None:
         kw = dict(segm_out=partials[0], segm_max=partials[1], segm_expsum=partials[2])

@@ -80,9 +80,9 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens, const int32_t* 
   if (N < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: N must be >= 1 (got %d)", N);
   if (R < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: R must be >= 1 (got %d)", R);
   if (W < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: W must be >= 1 (got %d)", W);
-  if (interleave != 1)
-    return fail(MLA_ERR_UNSUPPORTED,
-                "mla_verify_plan: only round-robin interleave 1 is supported (got %d)",
+  if (interleave < 1 || (int64_t)interleave * W > (1 << 30))
+    return fail(MLA_ERR_INVALID,
+                "mla_verify_plan: interleave must be >= 1 with interleave * W <= 2^30 (got %d)",
                 interleave);
   if (block_size <= 0)
     return fail(MLA_ERR_INVALID, "mla_verify_plan: block_size must be > 0 (got %d)", block_size);
@@ -107,7 +107,7 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens, const int32_t* 
     return fail(MLA_ERR_INVALID, "mla_verify_plan: null tensor argument");
 
   mla::PlanArgs a{};
-  a.N = N; a.R = R; a.W = W;
+  a.N = N; a.R = R; a.W = W; a.I = interleave;
   a.seq_lens = seq_lens; a.q_start = q_start; a.block_table = block_table;
   a.max_blocks = max_blocks; a.num_blocks = num_blocks;
   a.block_size = block_size; a.page_size = page_size;

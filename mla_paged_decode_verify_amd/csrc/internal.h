@@ -13,6 +13,7 @@ constexpr int kVDim = 512;
 
 struct PlanArgs {
   int32_t N, R, W;
+  int32_t I;                 // interleave: runs of I positions per shard
   const int32_t* seq_lens;
   const int32_t* q_start;
   const int32_t* block_table;

@@ -4,7 +4,12 @@
 // the _build_dcp_verify_row_view snippet -- verify row t of request i sees
 // global positions [0, S_i - Q_i + t]; with round-robin interleave 1 shard r
 // holds floor((w - 1 - r) / W) + 1 of the w = S_i - Q_i + 1 + t positions when
-// w - 1 - r >= 0 and none otherwise.
+// w - 1 - r >= 0 and none otherwise. With interleave I (runs of I consecutive
+// positions dealt to the shards in turn; the pages gate I > 1 off, this is a
+// reading of the same layout) a window of w positions is c = w div (I W) full
+// rounds plus rem = w mod (I W) positions, of which shard r gets
+// clamp(rem - r I, 0, I): L = c I + clamp(rem - r I, 0, I) (for I = 1 the
+// count above).
 // Sub-page table: same digest, item 3 -- the physical block table expanded to
 // sub-pages of page_size tokens (block b holds sub-pages b*n .. b*n + n - 1).
 //
@@ -20,11 +25,16 @@ namespace {
 
 constexpr int kPlanThreads = 256;
 
+// Positions of a window of w that shard r holds (w >= 0).
+__device__ __forceinline__ int64_t shard_count(int64_t w, int r, int W, int I) {
+  const int64_t cyc = (int64_t)I * W;
+  const int64_t c = w / cyc, rem = w - c * cyc;
+  return c * I + min(max(rem - (int64_t)r * I, (int64_t)0), (int64_t)I);
+}
 // Rows of shard r, row t of a request with window base S - Q (w = S - Q + 1 + t).
-__device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W) {
+__device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W, int I) {
   const int w = S - Q + 1 + t;       // window length of row t
-  const int d = w - 1 - r;           // explicit guard: C division truncates toward 0
-  return d >= 0 ? d / W + 1 : 0;
+  return w > 0 ? (int32_t)shard_count(w, r, W, I) : 0;
 }
 
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
@@ -38,7 +48,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   if (qs < 0 || qe > a.R || qe - qs < 1 || S < qe - qs) bits |= MLA_PLAN_ERR_QLEN;
   int64_t nb = 0;
   if (S >= 0) {
-    const int64_t local_max = ((int64_t)S + a.W - 1) / a.W;
+    const int64_t local_max = shard_count(S, 0, a.W, a.I);   // shard 0 holds the most
     if (local_max > a.max_kv_seq_len) bits |= MLA_PLAN_ERR_BOUND;
     nb = (local_max + a.block_size - 1) / a.block_size;
     if (nb > a.max_blocks) {
@@ -68,7 +78,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   if (nrows <= 0) return;
   for (int idx = tid; idx < a.W * nrows; idx += kPlanThreads) {
     const int r = idx / nrows, rho = r0 + idx % nrows;
-    a.row_lens[(int64_t)r * a.R + rho] = bits ? 0 : local_len(S, Q, rho - qs, r, a.W);
+    a.row_lens[(int64_t)r * a.R + rho] = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
     if (r == 0 && a.qo_indptr != nullptr) a.qo_indptr[rho] = rho;
   }
 
@@ -80,7 +90,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
     const int k = (int)(idx % a.pt_width);
     const int64_t row = idx / a.pt_width;
     const int r = (int)(row / nrows), rho = r0 + (int)(row % nrows);
-    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W);
+    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
     const int pages = (L + a.page_size - 1) / a.page_size;
     int32_t v = -1;
     if (k < pages) {

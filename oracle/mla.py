@@ -36,7 +36,7 @@ LOG2E = 1.0 / LN2
 __all__ = [
     "HEAD_DIM", "V_DIM", "LN2", "LOG2E",
     "subpage_size", "window_length", "row_view", "qo_indptr", "subpage_table",
-    "plan", "decode_bf16", "e4m3fn_value", "e4m3fn_table", "decode_e4m3fn",
+    "plan", "shard_of", "local_index", "decode_bf16", "e4m3fn_value", "e4m3fn_table", "decode_e4m3fn",
     "e5m2_value", "e5m2_table", "decode_e5m2",
     "gather_request_kv", "attention_rows", "shard_local_kv",
     "shard_attention_rows", "segment_partials", "segment_merge", "lse_merge",
@@ -83,15 +83,31 @@ def request_rows(q_start, i):
     return int(q_start[i]), int(q_start[i + 1]) - int(q_start[i])
 
 
-def row_view(seq_lens, q_start, W: int) -> np.ndarray:
+def shard_of(p, W: int, interleave: int = 1):
+    """Shard holding global position p under round-robin placement with the
+    given interleave: consecutive runs of `interleave` positions are dealt to
+    shards 0, 1, ..., W-1 in turn ([V51705] Implementation breakdown item 2
+    and [S34432] key snippet for interleave 1, where local index j of shard r
+    is global position j*W + r; interleave > 1 is this build's reading of the
+    same layout -- the pages gate it off as unverified)."""
+    return (np.asarray(p) // interleave) % W
+
+
+def local_index(p, W: int, interleave: int = 1):
+    """Index of global position p in its shard's local sequence: the run number
+    times the interleave plus the offset inside the run (j*W + r for
+    interleave 1). Increasing in p on every shard."""
+    p = np.asarray(p)
+    return (p // (interleave * W)) * interleave + p % interleave
+
+
+def row_view(seq_lens, q_start, W: int, interleave: int = 1) -> np.ndarray:
     """Rank-local KV length of every verify row on every shard, by brute force.
 
-    [V51705] Implementation breakdown item 2: with interleave 1, global
-    position p lives on shard p mod W (and [S34432] key snippet: local index j
-    of shard r is global position j*W + r). A row's local length on shard r is
-    the number of positions of its causal window that shard r holds. This
-    function counts them one position at a time; it does not use a closed
-    form. Returns int64 [W, R].
+    [V51705] Implementation breakdown item 2: a row's local length on shard r
+    is the number of positions of its causal window that shard r holds (see
+    shard_of). This function counts them one position at a time; it does not
+    use a closed form. Returns int64 [W, R].
     """
     seq_lens = [int(s) for s in seq_lens]
     q_start = [int(x) for x in q_start]
@@ -104,7 +120,7 @@ def row_view(seq_lens, q_start, W: int) -> np.ndarray:
             w = window_length(seq_lens[i], Q, t)
             if w <= 0:
                 continue
-            owner = np.arange(w, dtype=np.int64) % W  # shard of each position
+            owner = shard_of(np.arange(w, dtype=np.int64), W, interleave)
             out[:, qs + t] = np.bincount(owner, minlength=W)[:W]
     return out
 
@@ -149,7 +165,7 @@ def subpage_table(row_lens, block_table, q_start, block_size: int,
     return table
 
 
-def plan(seq_lens, q_start, W, block_table, block_size, max_kv_seq_len):
+def plan(seq_lens, q_start, W, block_table, block_size, max_kv_seq_len, interleave=1):
     """Everything the metadata builder produces, built once per forward.
 
     [V51705] key snippet, ``AiterMLADCPVerifyMetadata``: row lengths, the
@@ -157,7 +173,7 @@ def plan(seq_lens, q_start, W, block_table, block_size, max_kv_seq_len):
     The table width is ceil(max_kv_seq_len / page_size).
     """
     P = subpage_size(block_size)
-    L = row_view(seq_lens, q_start, W)
+    L = row_view(seq_lens, q_start, W, interleave)
     width = -(-int(max_kv_seq_len) // P)
     pt = subpage_table(L, block_table, q_start, block_size, P, width)
     return {"page_size": P, "row_lens": L, "page_table": pt,
@@ -240,7 +256,8 @@ def decode_e5m2(codes) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def gather_request_kv(cache, kv_dtype: str, kv_scale: float, block_table_row,
-                      seq_len: int, W: int, block_size: int) -> np.ndarray:
+                      seq_len: int, W: int, block_size: int,
+                      interleave: int = 1) -> np.ndarray:
     """Logical KV of one request, [S, 576] float64, read from the cache.
 
     ``cache`` holds raw bits, shaped [W, num_blocks, block_size, 576] (uint16
@@ -251,8 +268,8 @@ def gather_request_kv(cache, kv_dtype: str, kv_scale: float, block_table_row,
     per-tensor float scale, the same bytes serving K and V).
     """
     p = np.arange(int(seq_len), dtype=np.int64)
-    shard = p % W
-    local = p // W
+    shard = shard_of(p, W, interleave)
+    local = local_index(p, W, interleave)
     blocks = np.asarray(block_table_row, dtype=np.int64)[local // block_size]
     raw = cache[shard, blocks, local % block_size, :]
     if kv_dtype == "bf16":
@@ -295,9 +312,12 @@ def attention_rows(q_rows, K, seq_len: int, qlen: int, sm_scale: float):
     return out, lse
 
 
-def shard_local_kv(K, W: int, r: int):
-    """Shard r's local sequence: global positions r, r+W, r+2W, ..."""
-    return np.asarray(K)[r::W]
+def shard_local_kv(K, W: int, r: int, interleave: int = 1):
+    """Shard r's local sequence: its global positions in increasing order
+    (r, r+W, r+2W, ... for interleave 1)."""
+    K = np.asarray(K)
+    p = np.arange(K.shape[0])
+    return K[shard_of(p, W, interleave) == r]
 
 
 def shard_attention_rows(q_rows, K_local, L_rows, sm_scale: float):
@@ -461,7 +481,8 @@ def verify_reference(inp, requests=None):
         qs, Q = request_rows(q_start, i)
         K = gather_request_kv(inp["kv_bits"], inp["kv_dtype"], inp["kv_scale"],
                               inp["block_table"][i], int(seq_lens[i]),
-                              int(inp["W"]), int(inp["block_size"]))
+                              int(inp["W"]), int(inp["block_size"]),
+                              int(inp.get("interleave", 1)))
         o, l = attention_rows(q[qs:qs + Q], K, int(seq_lens[i]), Q,
                               float(inp["sm_scale"]))
         out[qs:qs + Q], lse[qs:qs + Q] = o, l

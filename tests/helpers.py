@@ -61,7 +61,7 @@ def run_gpu(inp, nseg=None, want_shards=False, stream=None):
 
 def oracle_plan(inp):
     return orc.plan(inp["seq_lens"], inp["q_start"], inp["W"], inp["block_table"],
-                    inp["block_size"], inp["max_kv_seq_len"])
+                    inp["block_size"], inp["max_kv_seq_len"], inp.get("interleave", 1))
 
 
 def max_err(a, b):
@@ -121,11 +121,12 @@ def oracle_shard_results(inp, plan, nseg):
     parts = {}
     for i in range(inp["N"]):
         qs, Q = orc.request_rows(inp["q_start"], i)
+        I = int(inp.get("interleave", 1))
         K = orc.gather_request_kv(inp["kv_bits"], inp["kv_dtype"], inp["kv_scale"],
                                   inp["block_table"][i], int(inp["seq_lens"][i]), W,
-                                  inp["block_size"])
+                                  inp["block_size"], I)
         for r in range(W):
-            local = orc.shard_local_kv(K, W, r)
+            local = orc.shard_local_kv(K, W, r, I)
             Lr = plan["row_lens"][r, qs:qs + Q]
             o, l = orc.shard_attention_rows(q[qs:qs + Q], local, Lr, inp["sm_scale"])
             so[r, qs:qs + Q], sl[r, qs:qs + Q] = o, l

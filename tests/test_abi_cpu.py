@@ -66,7 +66,8 @@ def _plan(**over):
 
 
 @pytest.mark.parametrize("over,code,msg", [
-    (dict(interleave=2), _lib.MLA_ERR_UNSUPPORTED, "interleave"),
+    (dict(interleave=0), _lib.MLA_ERR_INVALID, "interleave"),
+    (dict(interleave=1 << 29, W=4), _lib.MLA_ERR_INVALID, "interleave"),
     (dict(block_size=0, page_size=1), _lib.MLA_ERR_INVALID, "block_size"),
     (dict(page_size=32), _lib.MLA_ERR_INVALID, "page_size"),
     (dict(pt_width=1), _lib.MLA_ERR_INVALID, "pt_width"),

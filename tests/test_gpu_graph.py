@@ -68,3 +68,62 @@ def test_graph_replays_match_eager(kv_dtype, nseg):
                               eager["plan"]["row_lens"].cpu().numpy())
         assert torch.equal(out, ref_out)
         assert torch.equal(lse, ref_lse)
+
+
+def test_graph_static_bound_replays_new_lengths():
+    """Static-bound mode: the graph is captured once for fixed shapes and a
+    fixed max_kv_seq_len; before each replay the requests' lengths change in
+    place (every S_i between Q_i and its captured length). Each replay equals
+    an eager run on the new lengths bit for bit and matches the oracle: the
+    kernels read every length from device memory, so segments that lose their
+    tokens are simply inactive."""
+    import oracle as orc
+    from helpers import TOL_LSE, max_err, out_excess
+
+    spec = small_spec(N=4, W=3, qlen=4, seq_range=(200, 500), nseg=2)
+    inp = wl.make_workload(spec, seed=9)
+    dev = wl.to_device(inp)
+    nseg = spec["nseg"]
+    eager = mla.mla_verify_forward(dev, nseg=nseg)
+    torch.cuda.synchronize()
+    plan_bufs = {k: torch.empty_like(eager["plan"][k])
+                 for k in ("row_lens", "page_table", "qo_indptr")}
+    plan_bufs["err_flag"] = torch.zeros_like(eager["plan"]["err_flag"])
+    parts = tuple(torch.empty_like(p) for p in eager["partials"])
+    out, lse = torch.empty_like(eager["out"]), torch.empty_like(eager["lse"])
+
+    def step():
+        plan = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
+                                   dev["block_table"], dev["num_blocks"], dev["block_size"],
+                                   dev["max_kv_seq_len"], **plan_bufs)
+        mla.mla_verify_forward(dev, nseg=nseg, plan=plan, partials=parts, out=out, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(4)
+    S0, Q = inp["seq_lens"].copy(), inp["qlens"]
+    for rep in range(3):
+        S = np.array([int(rng.integers(q, s + 1)) for q, s in zip(Q, S0)], dtype=np.int64)
+        say(f"  replay {rep}: S={S.tolist()}")
+        dev["seq_lens"].copy_(torch.from_numpy(S.astype(np.int32)).to("cuda"))
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = mla.mla_verify_forward(dev, nseg=nseg)
+        torch.cuda.synchronize()
+        assert int(plan_bufs["err_flag"].item()) == 0
+        assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
+        inp_r = dict(inp, seq_lens=S)
+        out_ref, lse_ref = orc.verify_reference(inp_r)
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert out_excess(got, out_ref, "bf16") <= 1.0
+        assert max_err(lse.cpu().numpy().astype(np.float64), lse_ref) <= TOL_LSE

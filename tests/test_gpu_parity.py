@@ -52,6 +52,10 @@ SMALL = {
                               seq_range=(150, 900)),
     # e5m2 codes (the fp8_e5m2 cache dtype), 64- and 4-token sub-pages
     "e5m2_w4": small_spec(W=4, kv_dtype="fp8_e5m2", qlen=7, H=12, seq_range=(100, 600)),
+    # runs of I > 1 positions per shard (interleave)
+    "interleave2_w2": small_spec(W=2, interleave=2, qlen=5, seq_range=(60, 500)),
+    "interleave5_w3_b16": small_spec(W=3, interleave=5, block_size=16, qlen=4,
+                                     seq_range=(30, 400)),
     "e5m2_odd_block_p4": small_spec(W=3, block_size=12, kv_dtype="fp8_e5m2", qlen=2, H=8,
                                     seq_range=(40, 400)),
     "heads128_q8": small_spec(N=2, H=128, qlen=8, W=1, block_size=256, seq_range=(100, 300)),
@@ -112,6 +116,26 @@ def test_plan_fuzz_bit_exact(W, B):
         torch.cuda.synchronize()
         ref = orc.plan(inp["seq_lens"], inp["q_start"], W, inp["block_table"], B,
                        inp["max_kv_seq_len"] + seed * 17)
+        assert int(p["err_flag"].item()) == 0
+        assert np.array_equal(p["row_lens"].cpu().numpy(), ref["row_lens"])
+        assert np.array_equal(p["page_table"].cpu().numpy(), ref["page_table"])
+
+
+@pytest.mark.parametrize("W,B,I", [(2, 16, 2), (3, 48, 4), (4, 64, 3), (8, 16, 5), (2, 256, 64)])
+def test_plan_interleave_bit_exact(W, B, I):
+    """Row lengths and sub-page tables under interleave I against the oracle's
+    brute-force ownership count."""
+    for seed in range(3):
+        spec = dict(N=7, H=1, qlen_range=(1, 9), seq_range=(9, 700), block_size=B, W=W,
+                    interleave=I, kv_dtype="bf16", nseg=1)
+        inp = wl.make_workload(spec, seed=seed)
+        dev = wl.to_device(inp)
+        p = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], W,
+                                dev["block_table"], dev["num_blocks"], B,
+                                dev["max_kv_seq_len"], interleave=I)
+        torch.cuda.synchronize()
+        ref = orc.plan(inp["seq_lens"], inp["q_start"], W, inp["block_table"], B,
+                       inp["max_kv_seq_len"], I)
         assert int(p["err_flag"].item()) == 0
         assert np.array_equal(p["row_lens"].cpu().numpy(), ref["row_lens"])
         assert np.array_equal(p["page_table"].cpu().numpy(), ref["page_table"])

@@ -127,9 +127,9 @@ def test_qo_indptr():
 
 
 def _small_workload(seed=0, W=3, B=16, kv="bf16", N=4, H=2, seq=(20, 90), qlen=3,
-                    **kw):
+                    interleave=1, **kw):
     spec = dict(N=N, H=H, qlen=qlen, seq_range=seq, block_size=B, W=W,
-                kv_dtype=kv, nseg=1)
+                kv_dtype=kv, nseg=1, interleave=interleave)
     return wl.make_workload(spec, seed, keep_logical=True, **kw)
 
 
@@ -218,13 +218,13 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(ours[ok], lib[ok])
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3", "fp8_e5m2"])
-def test_gather_matches_generator_logical_kv(kv):
-    inp = _small_workload(seed=3, W=4, B=16, kv=kv)
+@pytest.mark.parametrize("kv,I", [("bf16", 1), ("fp8_e4m3", 1), ("fp8_e5m2", 1), ("bf16", 3)])
+def test_gather_matches_generator_logical_kv(kv, I):
+    inp = _small_workload(seed=3, W=4, B=16, kv=kv, interleave=I)
     for i in range(inp["N"]):
         got = orc.gather_request_kv(inp["kv_bits"], kv, inp["kv_scale"],
                                     inp["block_table"][i], inp["seq_lens"][i],
-                                    inp["W"], inp["block_size"])
+                                    inp["W"], inp["block_size"], I)
         assert np.array_equal(got, _logical_f64(inp, i))
         assert np.all(np.isfinite(got))
 
@@ -294,20 +294,21 @@ def test_attention_matches_torch_sdpa(S, Q, scale):
     assert np.allclose(out, lib_out, atol=1e-10, rtol=0)
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
-def test_sharded_then_merged_equals_unsharded(W):
+@pytest.mark.parametrize("W,I", [(1, 1), (2, 1), (3, 1), (4, 1), (8, 1), (2, 2), (3, 4), (4, 3)])
+def test_sharded_then_merged_equals_unsharded(W, I):
     """P5: per-shard rank-local attention over the row view, merged by
-    natural-log LSE, reproduces the unsharded definition."""
-    rng = np.random.default_rng(W)
+    natural-log LSE, reproduces the unsharded definition (also with runs of
+    I > 1 positions per shard)."""
+    rng = np.random.default_rng(W + 10 * I)
     for S, Q in [(1, 1), (5, 3), (29, 4), (70, 7)]:
         H = 2
         q = rng.standard_normal((Q, H, 576))
         K = rng.standard_normal((S, 576))
         out, lse = orc.attention_rows(q, K, S, Q, 0.1)
-        L = orc.row_view([S], [0, Q], W)
+        L = orc.row_view([S], [0, Q], W, I)
         outs, lses = [], []
         for r in range(W):
-            o, l = orc.shard_attention_rows(q, orc.shard_local_kv(K, W, r), L[r], 0.1)
+            o, l = orc.shard_attention_rows(q, orc.shard_local_kv(K, W, r, I), L[r], 0.1)
             outs.append(o)
             lses.append(l)
             for t in range(Q):
@@ -315,6 +316,41 @@ def test_sharded_then_merged_equals_unsharded(W):
         mo, ml = orc.lse_merge(np.stack(outs), np.stack(lses))
         assert np.allclose(mo, out, atol=1e-12, rtol=0)
         assert np.allclose(ml, lse, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("W,I", [(2, 2), (3, 2), (4, 3), (3, 5), (8, 4)])
+def test_interleaved_row_view_invariants(W, I):
+    """Runs of I consecutive positions dealt to the W shards in turn: every
+    window is split without loss (sum over shards = w), each shard's part is
+    a prefix of its local sequence (its first L positions are < w, the next
+    one is not), local indices number each shard's positions 0, 1, 2, ... in
+    increasing order, and I = 1 gives the round-robin closed form."""
+    rng = np.random.default_rng(7 * W + I)
+    for _ in range(10):
+        S = int(rng.integers(1, 120))
+        Q = int(rng.integers(1, min(S, 8) + 1))
+        L = orc.row_view([S], [0, Q], W, I)
+        pos = np.arange(S)
+        owner = orc.shard_of(pos, W, I)
+        loc = orc.local_index(pos, W, I)
+        for r in range(W):
+            mine = pos[owner == r]                  # increasing global positions
+            assert np.array_equal(loc[owner == r], np.arange(len(mine)))
+            for t in range(Q):
+                w = S - Q + 1 + t
+                n = int(L[r, t])
+                assert np.all(mine[:n] < w) and (n == len(mine) or mine[n] >= w)
+        for t in range(Q):
+            assert L[:, t].sum() == S - Q + 1 + t
+    # I >= every window: shard 0 holds all of it
+    L = orc.row_view([7], [0, 3], W, 7)
+    assert np.array_equal(L[0], [5, 6, 7]) and not np.any(L[1:])
+    # I = 1 is the round-robin count
+    L = orc.row_view([23], [0, 5], W, 1)
+    for r in range(W):
+        for t in range(5):
+            w = 23 - 5 + 1 + t
+            assert L[r, t] == ((w - 1 - r) // W + 1 if w - 1 - r >= 0 else 0)
 
 
 def test_two_stage_decomposition_equals_row_view():

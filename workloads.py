@@ -102,8 +102,11 @@ def make_workload(spec, seed: int = 0, *, q_mode: str = "normal",
     q_start[1:] = np.cumsum(qlens)
     R = int(q_start[-1])
 
-    # 3. paged storage: each request owns ceil(ceil(S/W)/B) blocks on every shard
-    local_max = -(-seq_lens // W)
+    # 3. paged storage: each request owns ceil(Lmax/B) blocks on every shard,
+    # Lmax its longest shard-local sequence (shard 0's): ceil(S/W) for
+    # interleave 1, c*I + min(S mod (I*W), I) with c = S div (I*W) in general
+    I = int(spec.get("interleave", 1))
+    local_max = (seq_lens // (I * W)) * I + np.minimum(seq_lens % (I * W), I)
     nblocks = -(-local_max // B)
     num_blocks = int(nblocks.sum()) + spare_blocks
     perm = torch.randperm(num_blocks, generator=g).numpy().astype(np.int64)
@@ -159,14 +162,15 @@ def make_workload(spec, seed: int = 0, *, q_mode: str = "normal",
         bits = per_req(i)
         S = int(seq_lens[i])
         p = np.arange(S)
-        j = p // W
-        cache[p % W, block_table[i][j // B], j % B, :] = bits
+        j = (p // (I * W)) * I + p % I                # local index on shard (p // I) % W
+        cache[(p // I) % W, block_table[i][j // B], j % B, :] = bits
         if keep_logical:
             logical.append(bits.copy())
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     return {
         "name": name, "seed": seed, "N": N, "H": H, "W": W, "block_size": B,
+        "interleave": I,
         "kv_dtype": kv_dtype, "kv_scale": float(kv_scale),
         "sm_scale": float(sm_scale), "nseg": int(spec.get("nseg", 1)),
         "seq_lens": seq_lens, "qlens": qlens, "q_start": q_start, "R": R,
@@ -209,6 +213,7 @@ def to_device(inp, device="cuda"):
         "q": q, "kv": kv, "seq_lens": i32(inp["seq_lens"]), "q_start": i32(inp["q_start"]),
         "block_table": i32(inp["block_table"]), "num_blocks": int(inp["num_blocks"]),
         "block_size": int(inp["block_size"]), "R": int(inp["R"]), "W": int(inp["W"]),
+        "interleave": int(inp.get("interleave", 1)),
         "max_kv_seq_len": int(inp["max_kv_seq_len"]), "max_qlen": int(np.max(inp["qlens"])),
         "sm_scale": float(inp["sm_scale"]), "kv_scale": float(inp["kv_scale"]),
     }

@@ -229,7 +229,75 @@ def mla_verify_forward(dev, *, nseg=1, plan=None, partials=None, out=None, lse=N
             "shard_lse": sl}
 
 
+def mla_verify_two_stage(dev, k_window, *, stream=None):
+    """The SGLang decomposition of the same verify result, from the same native
+    calls ([S34432] implementation item 3, the _forward_verify_dcp snippet):
+
+      stage 1 -- every shard attends over its part of the request's committed
+                 prefix [0, S_i - Q_i) (every verify row sees the same prefix);
+      stage 2 -- one shard attends over the dense causal window of the
+                 request's Q_i verify tokens (row t sees verify tokens 0..t),
+                 read from ``k_window`` [R, 576] bf16 (row rho = the entry of
+                 verify token rho, request-major, as the snippet lays it out);
+      merge   -- natural-log LSE merge over the W stage-1 shards and stage 2.
+
+    Both stages treat every verify row as a one-row request (q_start =
+    0..R), so one merge sees a consistent grouping; stage 2's pool is
+    ``k_window`` viewed as R blocks of one token. nseg is 1 (the two stages
+    have different sub-page sizes, and with one segment the partition does
+    not depend on them). A row whose request has no committed token has an
+    empty stage 1 (the plan flags it in a private error word). ``dev`` is a
+    dict as for mla_verify_forward. Returns (out, lse)."""
+    q, kv = dev["q"], dev["kv"]
+    R, H, _ = q.shape
+    W = dev["W"]
+    I = dev.get("interleave", 1)
+    d = q.device
+    i32 = dict(dtype=torch.int32, device=d)
+    _dev(k_window, torch.bfloat16, "k_window")
+    if tuple(k_window.shape) != (R, HEAD_DIM):
+        raise ValueError("k_window must be [R, 576]")
+    q_start = dev["q_start"].long()
+    N = q_start.shape[0] - 1
+    qlens = q_start[1:] - q_start[:-1]
+    req = torch.repeat_interleave(torch.arange(N, device=d), qlens)      # request of each row
+    t = torch.arange(R, device=d) - q_start[:-1][req]                    # row index in request
+    rows = torch.arange(R + 1, **i32)
+    # ---- stage 1: committed prefix, sharded
+    S1 = (dev["seq_lens"].long()[req] - qlens[req]).to(torch.int32).contiguous()
+    bt1 = dev["block_table"][req].contiguous()
+    row_lens = torch.empty((W + 1, R), **i32)
+    flag = torch.zeros((1,), **i32)
+    p1 = mla_verify_plan(S1, rows, R, W, bt1, dev["num_blocks"], dev["block_size"],
+                         dev["max_kv_seq_len"], interleave=I, row_lens=row_lens[:W],
+                         err_flag=flag, stream=stream)
+    parts = (torch.empty((W + 1, R, H, 1, V_DIM), dtype=torch.float32, device=d),
+             torch.empty((W + 1, R, H, 1), dtype=torch.float32, device=d),
+             torch.empty((W + 1, R, H, 1), dtype=torch.float32, device=d))
+    mla_verify_attn(q, kv, p1["row_lens"], p1["page_table"], rows, page_size=p1["page_size"],
+                    max_qlen=1, nseg=1, sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                    segm_out=parts[0][:W], segm_max=parts[1][:W], segm_expsum=parts[2][:W],
+                    stream=stream)
+    # ---- stage 2: dense causal window of the verify tokens, one shard
+    qmax = int(dev["max_qlen"])
+    bt2 = q_start[:-1][req].unsqueeze(1) + torch.arange(qmax, device=d).unsqueeze(0)
+    bt2 = torch.where(torch.arange(qmax, device=d).unsqueeze(0) < qlens[req].unsqueeze(1),
+                      bt2, torch.full_like(bt2, -1)).to(torch.int32).contiguous()
+    S2 = (t + 1).to(torch.int32).contiguous()
+    kv2 = k_window.view(1, R, 1, HEAD_DIM)
+    p2 = mla_verify_plan(S2, rows, R, 1, bt2, R, 1, qmax, row_lens=row_lens[W:],
+                         err_flag=flag, stream=stream)
+    mla_verify_attn(q, kv2, p2["row_lens"], p2["page_table"], rows, page_size=1, max_qlen=1,
+                    nseg=1, sm_scale=dev["sm_scale"], segm_out=parts[0][W:],
+                    segm_max=parts[1][W:], segm_expsum=parts[2][W:], stream=stream)
+    # ---- merge over the W + 1 partial sources
+    out, lse, _, _ = mla_lse_merge(*parts, row_lens, rows, page_size=1, H=H, nseg=1,
+                                   stream=stream)
+    return out, lse
+
+
 __all__ = [
     "mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes", "mla_verify_plan",
-    "mla_verify_attn", "mla_lse_merge", "mla_last_error", "mla_verify_forward", "MlaError", "HEAD_DIM", "V_DIM",
+    "mla_verify_attn", "mla_lse_merge", "mla_last_error", "mla_verify_forward",
+    "mla_verify_two_stage", "MlaError", "HEAD_DIM", "V_DIM",
 ]

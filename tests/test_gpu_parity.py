@@ -312,3 +312,40 @@ def test_merge_paths(name):
     say(f"  max|dout|={max_err(got['out'], out_ref):.3e} max|dlse|={max_err(got['lse'], lse_ref):.3e}")
     assert out_excess(got["out"], out_ref, "bf16") <= 1.0
     assert max_err(got["lse"], lse_ref) <= TOL_LSE
+
+
+# ------------------------------------------------------ two-stage variant ---
+
+@pytest.mark.parametrize("W,I", [(1, 1), (3, 1), (4, 2)])
+def test_two_stage_verify_matches_one_stage_and_oracle(W, I):
+    """The SGLang decomposition (sharded committed prefix + one-shard dense
+    causal window of the verify tokens, merged by LSE) built from the same
+    native calls gives the per-row-window result: against the oracle's
+    definition, its own two-stage decomposition, and the one-stage path.
+    Request 0 has no committed token (S = Q)."""
+    spec = dict(N=4, H=16, qlens=[5, 1, 3, 4], seq_lens=[5, 40, 233, 77], block_size=16, W=W,
+                interleave=I, kv_dtype="bf16", nseg=1)
+    inp = wl.make_workload(spec, seed=12, keep_logical=True)
+    say(f"two-stage W={W} I={I}")
+    dev = wl.to_device(inp)
+    win = np.concatenate([inp["logical_kv_bits"][i][int(S) - int(Q):int(S)]
+                          for i, (S, Q) in enumerate(zip(inp["seq_lens"], inp["qlens"]))])
+    k_window = torch.from_numpy(win.view(np.int16)).view(torch.bfloat16).to("cuda")
+    out2, lse2 = mla.mla_verify_two_stage(dev, k_window)
+    torch.cuda.synchronize()
+    got_out = out2.float().cpu().numpy().astype(np.float64)
+    got_lse = lse2.cpu().numpy().astype(np.float64)
+    out_ref, lse_ref = orc.verify_reference(inp)
+    assert out_excess(got_out, out_ref, "bf16") <= 1.0
+    assert max_err(got_lse, lse_ref) <= TOL_LSE
+    q = orc.decode_bf16(inp["q_bits"])
+    for i in range(inp["N"]):
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        K = orc.decode_bf16(inp["logical_kv_bits"][i])
+        o, l = orc.two_stage_verify(q[qs:qs + Q], K, int(inp["seq_lens"][i]), Q, W,
+                                    inp["sm_scale"])
+        assert out_excess(got_out[qs:qs + Q], o, "bf16") <= 1.0
+        assert max_err(got_lse[qs:qs + Q], l) <= TOL_LSE
+    one = run_gpu(inp)
+    assert out_excess(got_out, one["out"], "bf16") <= 1.0
+    assert max_err(got_lse, one["lse"]) <= TOL_LSE

@@ -5,7 +5,7 @@
 //  * Tiles go straight from HBM to LDS (global_load_lds_dwordx4: one 1 KB
 //    instruction per token's latent part, one per 8 tokens' rope parts), so no
 //    registers hold data in flight. While tile k is computed, tile k+1 streams
-//    in, issued two instructions per QK K-step over the first half of the QK
+//    in, issued one instruction per QK K-step over the first half of the QK
 //    work; two LDS buffers alternate.
 //  * Page-table entries: when sub-pages hold 16+ tokens, a wave's 16-token
 //    slice of a tile lies in one sub-page, so one vector load gives a wave the
@@ -42,7 +42,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 1;                  // row group: 32 rows
   const int c = wave & 1;                   // token half (QK) / latent half (PV)
-  const int r16 = lane & 15;
 
   const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kTokBytesBf16;
   const unsigned char* zero = zero_row();
@@ -72,14 +71,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
     issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane, zero);
   }
 
-  int mrow[2], hi_row[2];
-  bool row_ok[2];
-  lane_rows(a, u, g, r16, mrow, hi_row, row_ok);
+  int mrow, hi_row;
+  bool row_ok;
+  lane_row(a, u, g, lane, mrow, hi_row, row_ok);
   WaveState st;
   state_init(st);
   MLA_WAIT_VMCNT(0);
   lds_barrier();
-  bf16x8 qf[2][kQSteps];
+  bf16x8 qf[kQSteps];
   read_q(buf1, g, lane, qf);
 
   // One tile (index kt from the segment start): wait until `cur` holds it,
@@ -101,17 +100,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
         issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane, zero);
       }
     }
-    // two loads per QK K-step over the first nine K-steps: the next tile's
-    // data goes out early, without one long stall on issue
+    // one load per QK K-step over the first 18 K-steps: the next tile's data
+    // goes out early, without one long stall on issue
     auto issue = [&](int j) {
       if constexpr (SLICE) {
-        if (more && j < 9) {
-          issue_slice(v, zero, nxt, wave, lane, 2 * j);
-          issue_slice(v, zero, nxt, wave, lane, 2 * j + 1);
-        }
+        if (more && j < 18) issue_slice(v, zero, nxt, wave, lane, j);
       }
     };
-    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue, [] {});
+    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
   };
   int kt = 0;
   for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {

@@ -28,6 +28,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -40,9 +41,9 @@ constexpr int kRopeRow = 128;              // 64 bf16 rope = 8 chunks of 16 B
 constexpr int kRopeBytes = kTile * kRopeRow;
 constexpr int kBufBytes = kLatBytes + kRopeBytes;
 constexpr int kThreads = 256;
-constexpr int kQSteps = kHeadDim / 32;     // 18 MFMA K-steps (32 dims) for QK^T
-constexpr int kLatQSteps = kVDim / 32;     // the first 16 read the latent region
-constexpr int kNTiles = kVDim / 16;        // 32 output tiles of 16 latent dims
+constexpr int kQSteps = kHeadDim / 16;     // 36 MFMA K-steps (16 dims) for QK^T
+constexpr int kLatQSteps = kVDim / 16;     // the first 32 read the latent region
+constexpr int kOTiles = kVDim / 2 / 32;    // 8 output tiles of 32 latent dims per wave
 constexpr int kTokBytesBf16 = kHeadDim * 2;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;       // log2 units
@@ -63,21 +64,6 @@ __device__ __forceinline__ const unsigned char* zero_row() {
   const unsigned char* z = g_zero_token;
   asm volatile("" : "+s"(z));
   return z;
-}
-
-// max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane groups of a
-// wave), with the gfx950 lane-swap instructions instead of an LDS round trip.
-__device__ __forceinline__ float max4(float x) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-__device__ __forceinline__ float sum4(float x) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 // Address of token `tok` with sub-page id `sp`, or the zero row when the token
@@ -251,19 +237,6 @@ __device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
   return u;
 }
 
-// This lane's two rows (rows 32g + 16rt + l%16 of the block) and the part of
-// the segment each may see.
-__device__ inline void lane_rows(const AttnArgs& a, const WorkUnit& u, int g, int r16,
-                                 int (&mrow)[2], int (&hi_row)[2], bool (&row_ok)[2]) {
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    mrow[rt] = u.m0 + 32 * g + 16 * rt + r16;
-    row_ok[rt] = mrow[rt] < u.M;
-    const int Lrow = row_ok[rt] ? a.row_lens[(int64_t)u.r * a.R + u.qs + mrow[rt] / a.H] : 0;
-    hi_row[rt] = min(u.hi, Lrow);
-  }
-}
-
 // Q of the block, staged in a tile buffer: block row m (the (row, head) pair
 // m0 + m, one contiguous 1152-byte vector) is laid out like KV token m, so the
 // QK B-operand fragments are read exactly like K fragments. The block's pairs
@@ -293,47 +266,6 @@ __device__ __forceinline__ void issue_q_tile(const AttnArgs& a, const WorkUnit& 
   }
 }
 
-// K fragment (A operand of S^T = K Q^T) for K-step k: token `tok` of the tile,
-// 8 dims 32k + 8(l/16) .. +7 of lane l.
-__device__ __forceinline__ bf16x8 k_fragment(const unsigned char* tile, int tok, int k, int g4) {
-  if (k < kLatQSteps)
-    return *reinterpret_cast<const bf16x8*>(tile + lat_off(tok, 4 * k + g4));
-  const int chunk = 4 * (k - kLatQSteps) + g4;
-  return *reinterpret_cast<const bf16x8*>(tile + kLatBytes + tok * kRopeRow +
-                                          16 * (chunk ^ (tok & 7)));
-}
-
-// Q fragments (B operand of S^T = K Q^T) of this lane's rows from the staged
-// Q tile: 8 dims per lane per K-step. The reads are inline assembly that lands
-// them in accumulation registers, where the MFMAs take them as operands
-// directly (the compiler would otherwise keep them there and copy each one
-// back before every use); the trailing wait is tied to every fragment.
-__device__ __forceinline__ void read_q(const unsigned char* qtile, int g, int lane,
-                                       bf16x8 (&qf)[2][kQSteps]) {
-  const int g4 = lane >> 4;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = 32 * g + 16 * rt + (lane & 15);
-#pragma unroll
-    for (int k = 0; k < kQSteps; ++k) {
-      const unsigned char* p =
-          k < kLatQSteps ? qtile + lat_off(row, 4 * k + g4)
-                         : qtile + kLatBytes + row * kRopeRow +
-                               16 * ((4 * (k - kLatQSteps) + g4) ^ (row & 7));
-      const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
-      asm volatile("ds_read_b128 %0, %1" : "=a"(qf[rt][k]) : "v"(addr));
-    }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-    for (int k = 0; k < kQSteps; k += 6)
-      asm volatile("" : "+a"(qf[rt][k]), "+a"(qf[rt][k + 1]), "+a"(qf[rt][k + 2]),
-                        "+a"(qf[rt][k + 3]), "+a"(qf[rt][k + 4]), "+a"(qf[rt][k + 5]));
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Per-tile computation, shared by the bf16 and fp8 kernels.
 //
@@ -342,11 +274,21 @@ __device__ __forceinline__ void read_q(const unsigned char* qtile, int g, int la
 // dims 256c..256c+255 over all 64 tokens, so the two waves of a row group trade
 // their row maxima and their P fragments through LDS once per tile each.
 //
-// S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with Q in
-// registers. The S^T accumulator layout is already the B-operand layout of the
-// PV product (under a fixed token permutation inside each 32-token K-step), so
-// P never moves between the lanes of a wave; V^T fragments come straight from
-// the row-major tile with ds_read_b64_tr_b16 in the same permutation.
+// Both products run on v_mfma_f32_32x32x16_bf16 (a 32x32 output tile per
+// instruction: more flops per issue cycle than the 16x16 forms). Operand and
+// accumulator lanes of that instruction (h = l / 32):
+//   A (32 x 16): lane l holds A[l % 32][8h + e], e = 0..7
+//   B (16 x 32): lane l holds B[8h + e][l % 32]
+//   D (32 x 32): value j of lane l is D[8 (j / 4) + 4h + j % 4][l % 32]
+// So lane l owns one query row, 32g + l % 32, in both products.
+//  * S^T[32 tokens x 32 rows] = K Q^T: 36 K-steps of 16 dims, Q in registers.
+//    Accumulator value j is token 8 (j / 4) + 4h + j % 4 of the wave's 32.
+//  * O^T[256 dims x 32 rows] += V^T P^T: 8 output tiles of 32 dims, 4 K-steps
+//    of 16 tokens per tile. Values 8s..8s+7 of the S^T accumulator are tokens
+//    16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}: converted to bf16 they are
+//    already the B operand of the wave's own K-step s, so P never moves
+//    between lanes; the V^T operand takes the same token order from two
+//    transposed 4-token reads (ds_read_b64_tr_b16) per instruction.
 //
 // Online softmax in base 2 with a lazily refreshed reference: O and the sum
 // are rescaled only when the row maximum passes the reference by more than 8
@@ -354,167 +296,182 @@ __device__ __forceinline__ void read_q(const unsigned char* qtile, int g, int la
 // once to the true maximum, which is what is stored. Both waves of a row
 // group see the same tile maxima and so make the same decisions.
 
-// Accumulation state of one wave: 32 rows (two 16-row tiles) x 256 latent dims.
+// Accumulation state of one wave: 32 rows x 256 latent dims.
 struct WaveState {
-  f32x4 o[2][kNTiles / 2];  // O^T tiles: lane l holds dims 256c + 16n + 4(l/16) + 0..3
-  float m_ref[2];           // reference exponent of o and l_part (row-uniform)
-  float m_true[2];          // true running maximum (row-uniform)
-  float l_part[2];          // this lane's share of the exp2 sum over this wave's tokens
+  f32x16 o[kOTiles];        // O^T tiles: value j of lane l is dim 256c + 32t + 8(j/4) + 4h + j%4
+  float m_ref;              // this lane's row: reference exponent of o and l_part
+  float m_true;             // this lane's row: true running maximum
+  float l_part;             // this lane's share of the row's exp2 sum over this wave's tokens
 };
 
 // Row maxima and P fragments handed to the partner wave, once per tile each.
 struct PExchange {
-  uint4 p[2][2][2][64];     // [g][c][row tile][lane]: bf16 P of wave (g, c)'s tokens
-  float mx[2][2][2][16];    // [g][c][row tile][row]: its maxima over its tokens
+  uint4 p[2][2][2][64];     // [g][c][K-step of the wave's tokens][lane]: bf16 P
+  float mx[2][2][32];       // [g][c][row]: maxima over the wave's 32 tokens
 };
 
 // End-of-segment exchange of row sums between partner waves.
 struct RowExchange {
-  float l[2][2][2][16];     // [g][c][row tile][row]
+  float l[2][2][32];        // [g][c][row]
 };
 
 __device__ __forceinline__ void state_init(WaveState& st) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int t = 0; t < kOTiles; ++t) st.o[t] = f32x16{};
+  st.m_ref = kNegInf;
+  st.m_true = kNegInf;
+  st.l_part = 0.f;
+}
+
+// This lane's row (row 32g + l % 32 of the block) and the part of the segment
+// it may see.
+__device__ inline void lane_row(const AttnArgs& a, const WorkUnit& u, int g, int lane, int& mrow,
+                                int& hi_row, bool& row_ok) {
+  mrow = u.m0 + 32 * g + (lane & 31);
+  row_ok = mrow < u.M;
+  const int Lrow = row_ok ? a.row_lens[(int64_t)u.r * a.R + u.qs + mrow / a.H] : 0;
+  hi_row = min(u.hi, Lrow);
+}
+
+// K fragment (A operand of S^T = K Q^T) of K-step k: token `tok` of the tile,
+// dims 16k + 8h .. +7.
+__device__ __forceinline__ bf16x8 k_fragment(const unsigned char* tile, int tok, int k, int h) {
+  if (k < kLatQSteps)
+    return *reinterpret_cast<const bf16x8*>(tile + lat_off(tok, 2 * k + h));
+  const int chunk = 2 * (k - kLatQSteps) + h;
+  return *reinterpret_cast<const bf16x8*>(tile + kLatBytes + tok * kRopeRow +
+                                          16 * (chunk ^ (tok & 7)));
+}
+
+// Q fragments (B operand of S^T = K Q^T) of this lane's row from the staged Q
+// tile: dims 16k + 8h .. +7 for every K-step k. The reads are inline assembly
+// that lands them in accumulation registers, where the MFMAs take them as
+// operands directly (the compiler would otherwise keep them there and copy
+// each one back before every use); the trailing wait is tied to every
+// fragment.
+__device__ __forceinline__ void read_q(const unsigned char* qtile, int g, int lane,
+                                       bf16x8 (&qf)[kQSteps]) {
+  const int h = lane >> 5;
+  const int row = 32 * g + (lane & 31);
 #pragma unroll
-    for (int n = 0; n < kNTiles / 2; ++n) st.o[rt][n] = f32x4{};
-    st.m_ref[rt] = kNegInf;
-    st.m_true[rt] = kNegInf;
-    st.l_part[rt] = 0.f;
+  for (int k = 0; k < kQSteps; ++k) {
+    const unsigned char* p =
+        k < kLatQSteps ? qtile + lat_off(row, 2 * k + h)
+                       : qtile + kLatBytes + row * kRopeRow +
+                             16 * ((2 * (k - kLatQSteps) + h) ^ (row & 7));
+    const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
+    asm volatile("ds_read_b128 %0, %1" : "=a"(qf[k]) : "v"(addr));
   }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < kQSteps; k += 6)
+    asm volatile("" : "+a"(qf[k]), "+a"(qf[k + 1]), "+a"(qf[k + 2]), "+a"(qf[k + 3]),
+                      "+a"(qf[k + 4]), "+a"(qf[k + 5]));
 }
 
 // Scores, softmax and PV for one 64-token tile held in `tile` (LDS).
-// `issue(k)` is called once per QK K-step (k = 0..17), so that the loads of
-// the next tile can be spread over the MFMA work; `after_qk()` runs once the
-// Q fragments have been used for the last time in this tile.
-template <class Issue, class AfterQK>
+// `issue(k)` is called once per QK K-step (k = 0..35), so that the loads of
+// the next tile can be spread over the MFMA work.
+template <class Issue>
 __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ tile,
                                              PExchange* __restrict__ px,
-                                             const bf16x8 (&qf)[2][kQSteps],
-                                             WaveState& st, int tb, const int (&hi_row)[2],
-                                             float qk_scale_log2, int g, int c, int lane,
-                                             Issue&& issue, AfterQK&& after_qk) {
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
+                                             const bf16x8 (&qf)[kQSteps], WaveState& st, int tb,
+                                             int hi_row, float qk_scale_log2, int g, int c,
+                                             int lane, Issue&& issue) {
+  const int h = lane >> 5;
+  const int n32 = lane & 31;
 
-  // ---- S^T[32 tokens x 32 rows]: per K-step two K fragments (16 tokens each),
-  // each feeding both row tiles. Fragments are read kKAhead K-steps ahead of
-  // their MFMAs (a ring); the scheduling barriers keep that order.
+  // ---- S^T[32 tokens x 32 rows]; K fragments are read kKAhead K-steps ahead
+  // of their MFMAs (a ring); the scheduling barriers keep that order.
   constexpr int kKAhead = 2;
-  f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};  // [row tile][token tile]
-  bf16x8 kr[kKAhead + 1][2];
+  f32x16 sacc = f32x16{};
+  bf16x8 kr[kKAhead + 1];
 #pragma unroll
-  for (int k = 0; k < kKAhead; ++k) {
-    kr[k][0] = k_fragment(tile, 32 * c + r16, k, g4);
-    kr[k][1] = k_fragment(tile, 32 * c + 16 + r16, k, g4);
-  }
+  for (int k = 0; k < kKAhead; ++k) kr[k] = k_fragment(tile, 32 * c + n32, k, h);
 #pragma unroll
   for (int k = 0; k < kQSteps; ++k) {
-    if (k + kKAhead < kQSteps) {
-      kr[(k + kKAhead) % (kKAhead + 1)][0] = k_fragment(tile, 32 * c + r16, k + kKAhead, g4);
-      kr[(k + kKAhead) % (kKAhead + 1)][1] = k_fragment(tile, 32 * c + 16 + r16, k + kKAhead, g4);
-    }
+    if (k + kKAhead < kQSteps)
+      kr[(k + kKAhead) % (kKAhead + 1)] = k_fragment(tile, 32 * c + n32, k + kKAhead, h);
     issue(k);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k % (kKAhead + 1)][tt], qf[rt][k],
-                                                               sacc[rt][tt], 0, 0, 0);
-    }
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[k % (kKAhead + 1)], qf[k], sacc, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  after_qk();
 
-  // ---- mask, row maximum over this wave's 32 tokens. Element e of a row tile
-  // is token 32c + 16(e/4) + 4(l/16) + e%4. Tiles that every row of the wave
-  // sees whole skip the masking. The scores stay unscaled: the scale is
-  // positive, so the maximum of the rounded scaled scores is the rounded
-  // scaled maximum, and the scale goes into the exponent's fused multiply-add.
-  if (__builtin_amdgcn_ballot_w64(tb + kTile > hi_row[0] || tb + kTile > hi_row[1]) != 0) {
+  // ---- mask, maximum of this lane's 16 scores and of the other half's 16
+  // (lane l ^ 32 holds the same row). Tiles that every row of the wave sees
+  // whole skip the masking. The scores stay unscaled: the scale is positive,
+  // so the maximum of the rounded scaled scores is the rounded scaled
+  // maximum, and the scale goes into the exponent's fused multiply-add.
+  if (__builtin_amdgcn_ballot_w64(tb + kTile > hi_row) != 0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = tb + 32 * c + 16 * tt + 4 * g4 + v;
-          if (tok >= hi_row[rt]) sacc[rt][tt][v] = kNegInf;
-        }
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int tok = tb + 32 * c + 8 * (j >> 2) + 4 * h + (j & 3);
+      if (tok >= hi_row) sacc[j] = kNegInf;
     }
   }
-  float mx[2];
+  float m = sacc[0];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    mx[rt] = fmaxf(fmaxf(fmaxf(sacc[rt][0][0], sacc[rt][0][1]), fmaxf(sacc[rt][0][2], sacc[rt][0][3])),
-                   fmaxf(fmaxf(sacc[rt][1][0], sacc[rt][1][1]), fmaxf(sacc[rt][1][2], sacc[rt][1][3])));
-    mx[rt] = max4(mx[rt]);
-    if (g4 == 0) px->mx[g][c][rt][r16] = mx[rt];
+  for (int j = 1; j < 16; ++j) m = fmaxf(m, sacc[j]);
+  {
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
   }
+  if (h == 0) px->mx[g][c][n32] = m;
 
-  // ---- V^T reads for the first PV steps go out before the barrier. Lane i of
-  // each 16-lane group points at dims 16n + 4(i%4) of token t0 + i/4; the
-  // transposed read hands it dim 16n + i of tokens t0..t0+3. Step t covers
-  // 16-dim tile n = t % 16 and, for t < 16, the wave's own token half (K-step
-  // of the PV product: tokens 32c..32c+31), for t >= 16 the partner's; each
-  // step's two reads are issued kVAhead steps ahead of its MFMAs (a ring).
+  // ---- V^T reads for the first PV steps go out before the barrier. Step t
+  // covers output tile dt = t % 8 and K-step s: the wave's own tokens first
+  // (s = 2c + t / 8 for t < 16), then the partner's (s = 2(c ^ 1) + (t - 16) / 8).
+  // Lane i of 16-lane group (h, G) points at dims 256c + 32dt + 16G + 4(i % 4)
+  // of token 16s + 4h + i / 4 (and of the token 8 further); the transposed
+  // read hands it dim 256c + 32dt + 16G + i of tokens 16s + 4h + 0..3 (and
+  // 16s + 8 + 4h + 0..3). Each step's reads are issued kVAhead steps ahead of
+  // its MFMA (a ring).
   const int i16 = lane & 15;
+  const int G = (lane >> 4) & 1;
   auto vread = [&](int t, i16x4& lo4, i16x4& hi4) {
-    const int kk = t < 16 ? c : c ^ 1, n = t & 15;
-    const int row = 32 * kk + 4 * g4 + (i16 >> 2);
-    const int ch = 32 * c + 2 * n + ((i16 & 3) >> 1);
+    const int s = t < 16 ? 2 * c + (t >> 3) : 2 * (c ^ 1) + ((t - 16) >> 3);
+    const int dt = t & 7;
+    const int row = 16 * s + 4 * h + (i16 >> 2);
+    const int ch = 32 * c + 4 * dt + 2 * G + ((i16 & 3) >> 1);
     const int byte = 8 * (i16 & 1);
     lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + lat_off(row, ch) + byte));
     hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(tile + lat_off(row + 16, ch) + byte));
+        (lds_i16x4*)(tile + lat_off(row + 8, ch) + byte));
   };
-  constexpr int kPvSteps = 2 * (kNTiles / 2);
+  constexpr int kPvSteps = 4 * kOTiles;
   constexpr int kVAhead = 3;
   i16x4 vr[kVAhead + 1][2];
 #pragma unroll
   for (int t = 0; t < kVAhead; ++t) vread(t, vr[t][0], vr[t][1]);
 
   lds_barrier();
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    // the partner saw the other 32 tokens; both waves now hold the same tile max
-    mx[rt] = fmaxf(mx[rt], px->mx[g][c ^ 1][rt][r16]) * qk_scale_log2;
-    st.m_true[rt] = fmaxf(st.m_true[rt], mx[rt]);
-  }
+  // the partner saw the other 32 tokens; both waves now hold the same tile max
+  m = fmaxf(m, px->mx[g][c ^ 1][n32]) * qk_scale_log2;
+  st.m_true = fmaxf(st.m_true, m);
 
   // ---- lazily refreshed reference (identical decisions on both waves)
-  const bool refresh0 = mx[0] > st.m_ref[0] + kRescaleSlack;
-  const bool refresh1 = mx[1] > st.m_ref[1] + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(refresh0 || refresh1) != 0) {
+  const bool refresh = m > st.m_ref + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(refresh) != 0) {
+    const float alpha = refresh ? __builtin_amdgcn_exp2f(st.m_ref - m) : 1.f;
+    st.l_part *= alpha;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const bool rf = rt ? refresh1 : refresh0;
-      const float alpha = rf ? __builtin_amdgcn_exp2f(st.m_ref[rt] - mx[rt]) : 1.f;
-      st.l_part[rt] *= alpha;
-#pragma unroll
-      for (int n = 0; n < kNTiles / 2; ++n) st.o[rt][n] *= alpha;
-      st.m_ref[rt] = rf ? mx[rt] : st.m_ref[rt];
-    }
+    for (int t = 0; t < kOTiles; ++t) st.o[t] *= alpha;
+    st.m_ref = refresh ? m : st.m_ref;
   }
 
-  // ---- P of this wave's tokens; publish it for the partner
+  // ---- P of this wave's tokens (its two PV K-steps); publish it for the partner
+  const float m_use = st.m_ref == kNegInf ? 0.f : st.m_ref;
   bf16x8 pown[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const float m_use = st.m_ref[rt] == kNegInf ? 0.f : st.m_ref[rt];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // masked: the score is -inf and exp2(-inf) = 0 (m_use is finite)
-      const float p =
-          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rt][e >> 2][e & 3], qk_scale_log2, -m_use));
-      st.l_part[rt] += p;
-      pown[rt][e] = (__bf16)p;
-    }
-    px->p[g][c][rt][lane] = __builtin_bit_cast(uint4, pown[rt]);
+  for (int j = 0; j < 16; ++j) {
+    // masked: the score is -inf and exp2(-inf) = 0 (m_use is finite)
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], qk_scale_log2, -m_use));
+    st.l_part += p;
+    pown[j >> 3][j & 7] = (__bf16)p;
   }
+  px->p[g][c][0][lane] = __builtin_bit_cast(uint4, pown[0]);
+  px->p[g][c][1][lane] = __builtin_bit_cast(uint4, pown[1]);
   // The own half of the PV product needs only this wave's P: it runs while
   // the partner's P is on its way (the exchange barrier sits at step 16).
   bf16x8 ppart[2];
@@ -524,21 +481,19 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
   for (int t = 0; t < kPvSteps; ++t) {
     if (t == 16) {
       lds_barrier();
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        ppart[rt] = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][rt][lane]);
+      ppart[0] = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][0][lane]);
+      ppart[1] = __builtin_bit_cast(bf16x8, px->p[g][c ^ 1][1][lane]);
     }
     if (t + kVAhead < kPvSteps)
       vread(t + kVAhead, vr[(t + kVAhead) % (kVAhead + 1)][0], vr[(t + kVAhead) % (kVAhead + 1)][1]);
     __builtin_amdgcn_sched_barrier(0);
-    const int n = t & 15;
+    const int dt = t & 7;
+    const int sl = (t >> 3) & 1;            // K-step within the wave's (or partner's) tokens
     const bf16x8 va = __builtin_bit_cast(
         bf16x8, __builtin_shufflevector(vr[t % (kVAhead + 1)][0], vr[t % (kVAhead + 1)][1], 0, 1, 2,
                                         3, 4, 5, 6, 7));
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-      st.o[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, t < 16 ? pown[rt] : ppart[rt],
-                                                            st.o[rt][n], 0, 0, 0);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, t < 16 ? pown[sl] : ppart[sl], st.o[dt],
+                                                       0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -546,39 +501,41 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
 // End of the segment: add the partner wave's row sums and write the partials
 // (maximum, sum and O relative to the maximum). O goes through LDS (`stage`:
 // this row group's 32 rows, a tile buffer no longer read) so that the global
-// stores write whole rows, 1 KB per instruction, instead of 64-byte pieces.
-constexpr int kStageRow = 4 * kVDim + 16;   // padded: conflict-free row-tile writes
+// stores write whole rows, 1 KB per instruction, instead of 16-byte pieces.
+constexpr int kStageRow = 4 * kVDim + 16;   // padded row of 512 fp32
 static_assert(32 * kStageRow <= kBufBytes, "a row group's O fits a tile buffer");
 __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit& u,
                                                const WaveState& st, RowExchange& rx,
-                                               unsigned char* stage, const int (&mrow)[2],
-                                               const bool (&row_ok)[2], int g, int c,
-                                               int lane) {
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
-  float l_row[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    l_row[rt] = sum4(st.l_part[rt]);
-    if (g4 == 0) rx.l[g][c][rt][r16] = l_row[rt];
+                                               unsigned char* stage, int mrow, bool row_ok, int g,
+                                               int c, int lane) {
+  const int h = lane >> 5;
+  const int n32 = lane & 31;
+  float l_row;
+  {
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_part),
+                                              __float_as_uint(st.l_part), false, false);
+    l_row = __uint_as_float(q[0]) + __uint_as_float(q[1]);
   }
+  if (h == 0) rx.l[g][c][n32] = l_row;
   __syncthreads();                          // also: no wave reads a tile buffer any more
+  const float L = l_row + rx.l[g][c ^ 1][n32];
+  // move O and l from the reference exponent to the true maximum
+  float fix = 1.f;
+  if (st.m_true != kNegInf) fix = __builtin_amdgcn_exp2f(st.m_ref - st.m_true);
+  if (row_ok && c == 0 && h == 0) {
+    const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow) * a.nseg + u.s;
+    a.segm_max[e] = st.m_true;
+    a.segm_expsum[e] = L * fix;
+  }
+  const float vs = fix * a.v_scale;
+  float* sp = reinterpret_cast<float*>(stage + n32 * kStageRow) + 256 * c + 4 * h;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const float L = l_row[rt] + rx.l[g][c ^ 1][rt][r16];
-    // move O and l from the reference exponent to the true maximum
-    float fix = 1.f;
-    if (st.m_true[rt] != kNegInf) fix = __builtin_amdgcn_exp2f(st.m_ref[rt] - st.m_true[rt]);
-    const float vs = fix * a.v_scale;
-    if (row_ok[rt] && c == 0 && g4 == 0) {
-      const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow[rt]) * a.nseg + u.s;
-      a.segm_max[e] = st.m_true[rt];
-      a.segm_expsum[e] = L * fix;
+  for (int t = 0; t < kOTiles; ++t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = {st.o[t][4 * q], st.o[t][4 * q + 1], st.o[t][4 * q + 2], st.o[t][4 * q + 3]};
+      *reinterpret_cast<f32x4*>(sp + 32 * t + 8 * q) = v * vs;
     }
-    float* sp = reinterpret_cast<float*>(stage + (16 * rt + r16) * kStageRow) + 256 * c + 4 * g4;
-#pragma unroll
-    for (int n = 0; n < kNTiles / 2; ++n)
-      *reinterpret_cast<f32x4*>(sp + 16 * n) = st.o[rt][n] * vs;
   }
   __syncthreads();
   // wave (g, c) stores rows 16c .. 16c + 15 of its row group, half a row a go
@@ -590,9 +547,9 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
     const unsigned char* src = stage + (16 * c + k) * kStageRow + 16 * lane;
     float* dst = a.segm_out + e * kVDim + 4 * lane;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<float4*>(dst + 256 * h) =
-          *reinterpret_cast<const float4*>(src + 1024 * h);
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<float4*>(dst + 256 * hh) =
+          *reinterpret_cast<const float4*>(src + 1024 * hh);
   }
 }
 

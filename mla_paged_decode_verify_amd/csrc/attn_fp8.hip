@@ -136,7 +136,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 1;                  // row group: 32 rows
   const int c = wave & 1;                   // token half (QK) / latent half (PV)
-  const int r16 = lane & 15;
 
   const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kHeadDim;
   const unsigned char* zero = zero_row();
@@ -177,14 +176,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   // ---- tiles 0 and 1 in flight with Q; Q into registers; tile 0 widened
   issue_tile(0);
   if (ntiles > 1) issue_tile(1);
-  int mrow[2], hi_row[2];
-  bool row_ok[2];
-  lane_rows(a, u, g, r16, mrow, hi_row, row_ok);
+  int mrow, hi_row;
+  bool row_ok;
+  lane_row(a, u, g, lane, mrow, hi_row, row_ok);
   WaveState st;
   state_init(st);
   MLA_WAIT_VMCNT(0);
   lds_barrier();
-  bf16x8 qf[2][kQSteps];
+  bf16x8 qf[kQSteps];
   read_q(buf, g, lane, qf);
   lds_barrier();                            // every wave holds its Q: the buffer is free
   widen_tile<E5M2>(stage, buf, tid);
@@ -193,7 +192,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
 
   for (int k = 0; k < ntiles; ++k) {
     compute_tile(buf, &px, qf, st, lo + k * kTile, hi_row, a.qk_scale_log2, g, c, lane,
-                 [](int) {}, [] {});
+                 [](int) {});
     if (k + 1 < ntiles) {
       // tile k + 1 has landed (this wave's later loads: tile k + 2's nine)
       if (k + 2 < ntiles) MLA_WAIT_VMCNT(kF8Loads); else MLA_WAIT_VMCNT(0);

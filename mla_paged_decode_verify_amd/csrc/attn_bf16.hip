@@ -5,8 +5,8 @@
 //  * Tiles go straight from HBM to LDS (global_load_lds_dwordx4: one 1 KB
 //    instruction per token's latent part, one per 8 tokens' rope parts), so no
 //    registers hold data in flight. While tile k is computed, tile k+1 streams
-//    in, issued one instruction per QK K-step over the first half of the QK
-//    work; two LDS buffers alternate.
+//    in, issued one instruction every other QK K-step; two LDS buffers
+//    alternate.
 //  * Page-table entries: when sub-pages hold 16+ tokens, a wave's 16-token
 //    slice of a tile lies in one sub-page, so one vector load gives a wave the
 //    entries of 64 tiles (one per lane), read out with v_readlane; no load of
@@ -100,11 +100,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
         issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane, zero);
       }
     }
-    // one load per QK K-step over the first 18 K-steps: the next tile's data
-    // goes out early, without one long stall on issue
+    // one load every other QK K-step: the next tile's data goes out early,
+    // and its LDS writes are spread over the whole QK product, which competes
+    // with them for LDS bandwidth (measured: faster than packing the loads
+    // into the first half, or issuing them in the PV product)
     auto issue = [&](int j) {
       if constexpr (SLICE) {
-        if (more && j < 18) issue_slice(v, zero, nxt, wave, lane, j);
+        if (more && (j & 1) == 0) issue_slice(v, zero, nxt, wave, lane, j >> 1);
       }
     };
     compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);

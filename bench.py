@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA verify attention KV GB/s (% of HBM peak) + verify rows/sec at 1 GPU"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0          # dense bf16 (the fp8 path widens to bf16 before its MFMAs)
 
 
 def parse():
@@ -83,6 +84,27 @@ def stored_traffic(workload):
         return None
     try:
         return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def stored_mfma_flops(workload):
+    """Executed MFMA flops per attention launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
+    512) from the committed counter summary, or None if there is none for this
+    workload or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_mfma.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.split("(")[0].strip()] = v.split()[0] if v.split() else ""
+    if kv.get("source_sha256") != attn_source_hash():
+        return None
+    try:
+        return float(kv["executed_mfma_flops_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -272,6 +294,7 @@ def main():
     del cp, cq
     ms_step = wall * 1e3 / args.steps
     achieved = kv_bytes / (attn_launch_ms * 1e-3) / 1e9
+    mfma_flops = stored_mfma_flops(args.workload)
     res = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -306,6 +329,13 @@ def main():
                      "kernel": "attn_bf16_kernel" if inp["kv_dtype"] == "bf16" else "attn_fp8_kernel",
                      "bytes_per_launch": kv_bytes, "flops_per_launch": flops,
                      "frac_of_copy_peak": round(achieved / copy_gbs, 4)},
+        # the dense part: executed MFMA flops (from the committed counter
+        # summary, null once the kernel has changed) over this run's attention time
+        "mfma": None if mfma_flops is None else {
+            "executed_flops_per_launch": mfma_flops,
+            "achieved_tflops": round(mfma_flops / (attn_launch_ms * 1e-3) / 1e12, 1),
+            "peak_tflops": MFMA_PEAK_TFLOPS,
+            "util": round(mfma_flops / (attn_launch_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

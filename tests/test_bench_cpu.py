@@ -1,0 +1,40 @@
+"""Host-side checks of bench.py: the committed counter summaries it reads, and
+its refusal of more than one GPU. No GPU needed."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_traffic_summary_parses():
+    # the stored HBM traffic belongs to the verify workload; other workloads get None
+    t = bench.stored_traffic("verify_dcp8")
+    assert t is None or t > 0
+    assert bench.stored_traffic("ragged_mixed") is None
+
+
+def test_mfma_summaries_parse_and_agree_with_instruction_count():
+    for wl in ("verify_dcp8", "ragged_mixed"):
+        path = os.path.join(ROOT, "profiles", f"attn_{wl}_mfma.txt")
+        if not os.path.exists(path):
+            continue
+        f = bench.stored_mfma_flops(wl)
+        if f is None:              # summary taken before the kernel last changed
+            continue
+        # every v_mfma_f32_32x32x16_bf16 is 32768 flops: the executed count is a
+        # whole number of instructions
+        assert f > 0 and abs(f / 32768 - round(f / 32768)) < 1e-3 * (f / 32768)
+    assert bench.stored_mfma_flops("no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stdout + r.stderr

@@ -43,7 +43,7 @@ EXPORTED = {
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is not built; run `python -m mla_paged_decode_verify_amd.build` "
+            f"{path} is not built; run `python mla_paged_decode_verify_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(path)
     for name, (res, args) in EXPORTED.items():

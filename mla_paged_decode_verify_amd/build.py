@@ -1,6 +1,6 @@
 """Build the HIP library libmla_verify.so in-tree for gfx950 with hipcc.
 
-    python -m mla_paged_decode_verify_amd.build
+    python mla_paged_decode_verify_amd/build.py
 
 Every call recompiles. The shared library lands next to this file so that the
 Python binding (and anything that copies the source tree) finds it.

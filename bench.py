@@ -1,9 +1,13 @@
 #!/usr/bin/env python3
 """Throughput of the paged MLA verify hot path on one MI355X.
 
-One step = plan (row lengths + sub-page tables) -> split-K attention partials
--> segment + shard LSE merge, over one batch of the workload, inputs resident
-in HBM. The KV cache is rotated over several copies (more than the 256 MB
+One step = plan (row lengths + sub-page tables) -> attention -> merge, over
+one batch of the workload, inputs resident in HBM. With one segment per
+(request, shard) group (--path shards, the default then) the attention kernel
+folds the segment merge in and writes each shard's bf16 output + LSE, and the
+merge is the shard LSE merge alone; with split-K (--path split, the default
+for nseg > 1) the attention writes fp32 segment partials and the merge does
+the segment and the shard merge. The KV cache is rotated over several copies (more than the 256 MB
 Infinity Cache holds) so that no step re-reads the previous step's KV from
 cache. Timed steps launch the three calls from Python; --graph replays a HIP
 graph of them instead (one graph per KV copy; on this stack a replay costs more
@@ -40,6 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="verify_dcp8")
     ap.add_argument("--nseg", type=int, default=None)
+    ap.add_argument("--path", choices=["auto", "split", "shards"], default="auto",
+                    help="split: attn partials -> lse_merge; shards: attn_shard -> "
+                         "shard_merge (nseg 1 only); auto: shards when nseg is 1")
     ap.add_argument("--kv-copies", type=int, default=0,
                     help="KV copies to rotate over (0: enough for > 512 MB)")
     ap.add_argument("--graph", action="store_true",
@@ -150,6 +157,9 @@ def main():
 
     inp = wl.make_workload(args.workload, 0)
     nseg = inp["nseg"] if args.nseg is None else args.nseg
+    path = args.path if args.path != "auto" else ("shards" if nseg == 1 else "split")
+    if path == "shards" and nseg != 1:
+        raise SystemExit("--path shards needs nseg 1")
     dev = wl.to_device(inp)
     kv_bytes = wl.algorithmic_kv_bytes(inp)
     flops = wl.algorithmic_flops(inp)
@@ -166,8 +176,24 @@ def main():
                      page_table=torch.empty((W, R, ptw), **i32),
                      qo_indptr=torch.empty((R + 1,), **i32), err_flag=torch.zeros((1,), **i32))
     f32 = dict(dtype=torch.float32, device="cuda")
-    parts = (torch.empty((W, R, H, nseg, 512), **f32), torch.empty((W, R, H, nseg), **f32),
-             torch.empty((W, R, H, nseg), **f32))
+    if path == "split":
+        parts = (torch.empty((W, R, H, nseg, 512), **f32), torch.empty((W, R, H, nseg), **f32),
+                 torch.empty((W, R, H, nseg), **f32))
+    else:
+        parts = (torch.empty((W, R, H, 512), dtype=torch.bfloat16, device="cuda"),
+                 torch.empty((W, R, H), **f32))
+
+    def attn(kv, row_lens, page_table, bufs):
+        if path == "split":
+            mla.mla_verify_attn(dev["q"], kv, row_lens, page_table, dev["q_start"],
+                                page_size=page_size, max_qlen=dev["max_qlen"], nseg=nseg,
+                                sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                                segm_out=bufs[0], segm_max=bufs[1], segm_expsum=bufs[2])
+        else:
+            mla.mla_verify_attn_shard(dev["q"], kv, row_lens, page_table, dev["q_start"],
+                                      page_size=page_size, max_qlen=dev["max_qlen"],
+                                      sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                                      shard_out=bufs[0], shard_lse=bufs[1])
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((R, H), **f32)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -179,13 +205,13 @@ def main():
                                    dev["num_blocks"], inp["block_size"], inp["max_kv_seq_len"],
                                    **plan_bufs)
         if e: e[1].record()
-        mla.mla_verify_attn(dev["q"], kvs[k % len(kvs)], plan["row_lens"], plan["page_table"],
-                            dev["q_start"], page_size=page_size, max_qlen=dev["max_qlen"],
-                            nseg=nseg, sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
-                            segm_out=parts[0], segm_max=parts[1], segm_expsum=parts[2])
+        attn(kvs[k % len(kvs)], plan["row_lens"], plan["page_table"], parts)
         if e: e[2].record()
-        mla.mla_lse_merge(*parts, plan["row_lens"], dev["q_start"], page_size=page_size, H=H,
-                          nseg=nseg, out=out, lse=lse)
+        if path == "split":
+            mla.mla_lse_merge(*parts, plan["row_lens"], dev["q_start"], page_size=page_size,
+                              H=H, nseg=nseg, out=out, lse=lse)
+        else:
+            mla.mla_shard_merge(*parts, out=out, lse=lse)
         if e: e[3].record()
 
     if args.copy_calibration > 0:
@@ -243,11 +269,7 @@ def main():
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
     for k in range(n_attn):
-        mla.mla_verify_attn(dev["q"], kvs[k % len(kvs)], plan_bufs["row_lens"],
-                            plan_bufs["page_table"], dev["q_start"], page_size=page_size,
-                            max_qlen=dev["max_qlen"], nseg=nseg, sm_scale=dev["sm_scale"],
-                            kv_scale=dev["kv_scale"], segm_out=parts[0], segm_max=parts[1],
-                            segm_expsum=parts[2])
+        attn(kvs[k % len(kvs)], plan_bufs["row_lens"], plan_bufs["page_table"], parts)
     a1.record()
     torch.cuda.synchronize()
     attn_launch_ms = a0.elapsed_time(a1) / n_attn
@@ -261,13 +283,9 @@ def main():
     shard_us = None
     if W > 1:
         kv0 = [kv[0:1] for kv in kvs]
-        p0 = (torch.empty((1, R, H, nseg, 512), **f32), torch.empty((1, R, H, nseg), **f32),
-              torch.empty((1, R, H, nseg), **f32))
+        p0 = tuple(b[0:1] for b in parts)
         rl0, pt0 = plan_bufs["row_lens"][0:1], plan_bufs["page_table"][0:1]
-        attn0 = lambda k: mla.mla_verify_attn(
-            dev["q"], kv0[k % len(kv0)], rl0, pt0, dev["q_start"], page_size=page_size,
-            max_qlen=dev["max_qlen"], nseg=nseg, sm_scale=dev["sm_scale"],
-            kv_scale=dev["kv_scale"], segm_out=p0[0], segm_max=p0[1], segm_expsum=p0[2])
+        attn0 = lambda k: attn(kv0[k % len(kv0)], rl0, pt0, p0)
         for k in range(3):
             attn0(k)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -309,7 +327,7 @@ def main():
                    "qlen": int(np.max(inp["qlens"])), "rows": R, "shards": W,
                    "block_size": inp["block_size"], "page_size": page_size, "nseg": nseg,
                    "kv_dtype": inp["kv_dtype"], "sum_seq_len": int(inp["seq_lens"].sum()),
-                   "kv_copies": len(kvs)},
+                   "kv_copies": len(kvs), "path": path},
         "rows_per_s": round(R / (ms_step * 1e-3), 1),
         "hbm_frac": round(kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "launch": "hip_graph" if args.graph else "eager",
@@ -320,7 +338,7 @@ def main():
                           "kv_gbs_median": round(kv_bytes / (float(np.median(am)) * 1e-6) / 1e9, 1)},
         "shard0_alone_attn_us": None if shard_us is None else round(shard_us, 2),
         "bytes": {"kv_algorithmic": kv_bytes, "q": R * H * 1152, "out": R * H * (1024 + 4),
-                  "partials": W * R * H * nseg * (2048 + 8)},
+                  "partials": W * R * H * (nseg * (2048 + 8) if path == "split" else 1024 + 4)},
         "t_roof_us": round(max(kv_bytes / (HBM_PEAK_GBS * 1e9), flops / 2.5e15) * 1e6, 2),
         "hbm_copy_peak_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -178,6 +178,36 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
                              float* segm_expsum, void* stream);
 
 /*
+ * One-segment attention with the segment merge folded in: for every shard,
+ * row and head, the shard's normalised output and natural-log LSE over the
+ * part of the row's window that the shard holds ([V51705] Implementation
+ * breakdown item 4 with a single segment per (request, shard) group, whose
+ * merge is the normalisation; [S34432] report: a DCP rank hands its peers
+ * exactly this pair, bf16 output plus natural-log LSE). The same as
+ * mla_verify_attn with nseg = 1 followed by the per-shard part of
+ * mla_lse_merge, without the fp32 partials in between:
+ *   o_r = O / e rounded to bf16,  lse_r = ln2 * (m2 + log2 e),
+ * and o_r = 0, lse_r = -inf for a row with no token on shard r.
+ *
+ *   q, kv, num_blocks, block_size, page_size, kv_dtype, kv_scale, sm_scale,
+ *   row_lens, page_table, pt_width, q_start, N, R, H, W, max_qlen:
+ *              as for mla_verify_attn (same checks, same error codes)
+ * Outputs (device, caller-allocated):
+ *   shard_out  [W, R, H, 512] bf16, 16-byte aligned
+ *   shard_lse  [W, R, H] fp32
+ */
+mla_status_t mla_verify_attn_shard(const void* q, const void* kv,
+                                   int64_t num_blocks, int32_t block_size,
+                                   int32_t page_size, mla_kv_dtype_t kv_dtype,
+                                   float kv_scale, float sm_scale,
+                                   const int32_t* row_lens,
+                                   const int32_t* page_table, int32_t pt_width,
+                                   const int32_t* q_start, int32_t N, int32_t R,
+                                   int32_t H, int32_t W, int32_t max_qlen,
+                                   void* shard_out, float* shard_lse,
+                                   void* stream);
+
+/*
  * Segment merge then shard merge ([V51705] merge snippet and Implementation
  * breakdown item 4; [S34432] review item 4 for the natural-log convention).
  * Per shard r, over its active segments (s*T*P < that row's length):
@@ -200,6 +230,24 @@ mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
                            int32_t R, int32_t H, int32_t W, int32_t nseg,
                            void* shard_out, float* shard_lse, void* out,
                            float* lse, void* stream);
+
+/*
+ * Shard merge alone ([V51705] Motivation: rank-local results combine through
+ * the DCP attention merge; [S34432] review item 4: natural-log LSE):
+ *   lse = ln sum_r exp(lse_r),  out = sum_r exp(lse_r - lse) * o_r  -> bf16,
+ * shards with lse_r = -inf ignored; out = 0 and lse = -inf when every shard
+ * is empty. Gives the same bits as the shard step of mla_lse_merge.
+ *
+ *   shard_out  [W, R, H, 512] bf16 (e.g. from mla_verify_attn_shard),
+ *              16-byte aligned
+ *   shard_lse  [W, R, H] fp32
+ *   W          1 .. 1024 (MLA_ERR_UNSUPPORTED above)
+ *   out        [R, H, 512] bf16, 16-byte aligned
+ *   lse        [R, H] fp32
+ */
+mla_status_t mla_shard_merge(const void* shard_out, const float* shard_lse,
+                             int32_t R, int32_t H, int32_t W, void* out,
+                             float* lse, void* stream);
 
 /* Description of the last error on the calling thread ("" if none). */
 const char* mla_last_error(void);

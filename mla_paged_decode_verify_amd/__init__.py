@@ -163,6 +163,66 @@ def mla_verify_attn(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen
     return segm_out, segm_max, segm_expsum
 
 
+def mla_verify_attn_shard(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen,
+                          sm_scale, kv_scale=1.0, shard_out=None, shard_lse=None,
+                          stream=None):
+    """One-segment attention with the segment merge folded in: per shard, row
+    and head the normalised bf16 output and natural-log LSE. Arguments as for
+    mla_verify_attn. Returns (shard_out [W,R,H,512] bf16, shard_lse [W,R,H])."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(kv, None, "kv")
+    kvd = _kv_dtype(kv)
+    _dev(row_lens, torch.int32, "row_lens")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(q_start, torch.int32, "q_start")
+    R, H, D = q.shape
+    W, num_blocks, block_size, D2 = kv.shape
+    if D != HEAD_DIM or D2 != HEAD_DIM:
+        raise ValueError("head dim must be 576")
+    if tuple(row_lens.shape) != (W, R) or page_table.shape[:2] != (W, R):
+        raise ValueError("plan tensors do not match q / kv")
+    N = q_start.shape[0] - 1
+    dev = q.device
+    if shard_out is None:
+        shard_out = torch.empty((W, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if shard_lse is None:
+        shard_lse = torch.empty((W, R, H), dtype=torch.float32, device=dev)
+    _dev(shard_out, torch.bfloat16, "shard_out")
+    _dev(shard_lse, torch.float32, "shard_lse")
+    if shard_out.numel() != W * R * H * V_DIM or shard_lse.numel() != W * R * H:
+        raise ValueError("shard_out / shard_lse have the wrong size")
+    _check(_lib.lib.mla_verify_attn_shard(
+        _ptr(q), _ptr(kv), num_blocks, block_size, page_size, kvd, float(kv_scale),
+        float(sm_scale), _ptr(row_lens), _ptr(page_table), page_table.shape[2],
+        _ptr(q_start), N, R, H, W, int(max_qlen), _ptr(shard_out), _ptr(shard_lse),
+        _stream(stream)))
+    return shard_out, shard_lse
+
+
+def mla_shard_merge(shard_out, shard_lse, *, out=None, lse=None, stream=None):
+    """Shard LSE merge of per-shard bf16 outputs [W,R,H,512] and natural-log
+    LSEs [W,R,H]. Returns (out [R,H,512] bf16, lse [R,H] fp32)."""
+    _dev(shard_out, torch.bfloat16, "shard_out")
+    _dev(shard_lse, torch.float32, "shard_lse")
+    if shard_out.dim() != 4 or shard_out.shape[3] != V_DIM:
+        raise ValueError("shard_out must be [W, R, H, 512]")
+    W, R, H, _ = shard_out.shape
+    if tuple(shard_lse.shape) != (W, R, H):
+        raise ValueError("shard_lse must be [W, R, H]")
+    dev = shard_out.device
+    if out is None:
+        out = torch.empty((R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    _dev(out, torch.bfloat16, "out")
+    _dev(lse, torch.float32, "lse")
+    if out.numel() != R * H * V_DIM or lse.numel() != R * H:
+        raise ValueError("out / lse have the wrong size")
+    _check(_lib.lib.mla_shard_merge(_ptr(shard_out), _ptr(shard_lse), R, H, W, _ptr(out),
+                                    _ptr(lse), _stream(stream)))
+    return out, lse
+
+
 def mla_lse_merge(segm_out, segm_max, segm_expsum, row_lens, q_start, *, page_size,
                   H, nseg, out=None, lse=None, shard_out=None, shard_lse=None,
                   want_shards=False, stream=None):
@@ -227,6 +287,29 @@ def mla_verify_forward(dev, *, nseg=1, plan=None, partials=None, out=None, lse=N
                                  out=out, lse=lse, want_shards=want_shards, stream=stream)
     return {"plan": plan, "partials": parts, "out": o, "lse": l, "shard_out": so,
             "shard_lse": sl}
+
+
+def mla_verify_forward_shards(dev, *, plan=None, shards=None, out=None, lse=None,
+                              stream=None):
+    """plan -> one-segment attention (per-shard bf16 output + LSE) -> shard
+    merge, for the same dict as mla_verify_forward; the result equals
+    mla_verify_forward with nseg = 1. ``shards`` may pass (shard_out,
+    shard_lse) buffers. Returns a dict with the plan, shard_out, shard_lse,
+    out and lse."""
+    if plan is None:
+        plan = mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
+                               dev["block_table"], dev["num_blocks"], dev["block_size"],
+                               dev["max_kv_seq_len"], interleave=dev.get("interleave", 1),
+                               stream=stream)
+    kw = {}
+    if shards is not None:
+        kw = dict(shard_out=shards[0], shard_lse=shards[1])
+    so, sl = mla_verify_attn_shard(dev["q"], dev["kv"], plan["row_lens"], plan["page_table"],
+                                   dev["q_start"], page_size=plan["page_size"],
+                                   max_qlen=dev["max_qlen"], sm_scale=dev["sm_scale"],
+                                   kv_scale=dev["kv_scale"], stream=stream, **kw)
+    o, l = mla_shard_merge(so, sl, out=out, lse=lse, stream=stream)
+    return {"plan": plan, "shard_out": so, "shard_lse": sl, "out": o, "lse": l}
 
 
 def mla_verify_two_stage(dev, k_window, *, stream=None):
@@ -298,6 +381,7 @@ def mla_verify_two_stage(dev, k_window, *, stream=None):
 
 __all__ = [
     "mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes", "mla_verify_plan",
-    "mla_verify_attn", "mla_lse_merge", "mla_last_error", "mla_verify_forward",
+    "mla_verify_attn", "mla_lse_merge", "mla_verify_attn_shard", "mla_shard_merge",
+    "mla_last_error", "mla_verify_forward", "mla_verify_forward_shards",
     "mla_verify_two_stage", "MlaError", "HEAD_DIM", "V_DIM",
 ]

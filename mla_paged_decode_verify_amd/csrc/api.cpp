@@ -117,26 +117,31 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens, const int32_t* 
   return hip_status(mla::launch_plan(a, (hipStream_t)stream), "mla_verify_plan launch");
 }
 
-mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
-                             int32_t block_size, int32_t page_size, mla_kv_dtype_t kv_dtype,
-                             float kv_scale, float sm_scale, const int32_t* row_lens,
-                             const int32_t* page_table, int32_t pt_width,
-                             const int32_t* q_start, int32_t N, int32_t R, int32_t H,
-                             int32_t W, int32_t max_qlen, int32_t nseg, float* segm_out,
-                             float* segm_max, float* segm_expsum, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both attention entry points; fills everything in `a` but
+// the outputs. `fn` names the entry point in error messages.
+mla_status_t attn_args(const char* fn, const void* q, const void* kv, int64_t num_blocks,
+                       int32_t block_size, int32_t page_size, mla_kv_dtype_t kv_dtype,
+                       float kv_scale, float sm_scale, const int32_t* row_lens,
+                       const int32_t* page_table, int32_t pt_width, const int32_t* q_start,
+                       int32_t N, int32_t R, int32_t H, int32_t W, int32_t max_qlen,
+                       int32_t nseg, mla::AttnArgs& a, bool& fp8) {
   if (N < 1 || R < 1 || H < 1 || W < 1)
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: N, R, H, W must be >= 1 (got %d, %d, %d, %d)",
-                N, R, H, W);
-  if (nseg < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: nseg must be >= 1 (got %d)", nseg);
-  if (max_qlen < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: max_qlen must be >= 1");
+    return fail(MLA_ERR_INVALID, "%s: N, R, H, W must be >= 1 (got %d, %d, %d, %d)", fn, N, R,
+                H, W);
+  if (nseg < 1) return fail(MLA_ERR_INVALID, "%s: nseg must be >= 1 (got %d)", fn, nseg);
+  if (max_qlen < 1) return fail(MLA_ERR_INVALID, "%s: max_qlen must be >= 1", fn);
   if (block_size <= 0 || page_size != subpage_size(block_size))
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: page_size %d does not match block_size %d",
+    return fail(MLA_ERR_INVALID, "%s: page_size %d does not match block_size %d", fn,
                 page_size, block_size);
-  if (num_blocks < 1) return fail(MLA_ERR_INVALID, "mla_verify_attn: num_blocks must be >= 1");
-  if (pt_width < 0) return fail(MLA_ERR_INVALID, "mla_verify_attn: pt_width must be >= 0");
+  if (num_blocks < 1) return fail(MLA_ERR_INVALID, "%s: num_blocks must be >= 1", fn);
+  if (pt_width < 0) return fail(MLA_ERR_INVALID, "%s: pt_width must be >= 0", fn);
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_FP8_E5M2)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_verify_attn: unknown kv_dtype %d", (int)kv_dtype);
-  const bool fp8 = kv_dtype != MLA_KV_BF16;
+    return fail(MLA_ERR_UNSUPPORTED, "%s: unknown kv_dtype %d", fn, (int)kv_dtype);
+  fp8 = kv_dtype != MLA_KV_BF16;
   const double log2e = 1.4426950408889634;
   const float qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)kv_scale : 1.0) * log2e);
   // the kernels take the row maximum of unscaled scores, which needs a
@@ -144,17 +149,16 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale) ||
       (fp8 && (!(kv_scale > 0.f) || !std::isfinite(kv_scale))) || !(qk_scale_log2 > 0.f) ||
       !std::isfinite(qk_scale_log2))
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: scales must be positive and finite");
-  if (!q || !kv || !row_lens || !q_start || !segm_out || !segm_max || !segm_expsum ||
-      (pt_width > 0 && !page_table))
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: null tensor argument");
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(segm_out))
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: q, kv and segm_out must be 16-byte aligned");
+    return fail(MLA_ERR_INVALID, "%s: scales must be positive and finite", fn);
+  if (!q || !kv || !row_lens || !q_start || (pt_width > 0 && !page_table))
+    return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+  if (!aligned16(q) || !aligned16(kv))
+    return fail(MLA_ERR_INVALID, "%s: q and kv must be 16-byte aligned", fn);
   const int64_t mblocks = ((int64_t)max_qlen * H + mla::kAttnRows - 1) / mla::kAttnRows;
   if ((int64_t)N * W * nseg * mblocks > 0x7FFFFFFFLL)
-    return fail(MLA_ERR_INVALID, "mla_verify_attn: grid too large");
+    return fail(MLA_ERR_INVALID, "%s: grid too large", fn);
 
-  mla::AttnArgs a{};
+  a = mla::AttnArgs{};
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint8_t*>(kv);
   a.pool_tokens = num_blocks * block_size;
@@ -167,8 +171,55 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
   a.qk_scale_log2 = qk_scale_log2;
   a.v_scale = fp8 ? kv_scale : 1.0f;
   a.e5m2 = kv_dtype == MLA_KV_FP8_E5M2 ? 1 : 0;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
+                             int32_t block_size, int32_t page_size, mla_kv_dtype_t kv_dtype,
+                             float kv_scale, float sm_scale, const int32_t* row_lens,
+                             const int32_t* page_table, int32_t pt_width,
+                             const int32_t* q_start, int32_t N, int32_t R, int32_t H,
+                             int32_t W, int32_t max_qlen, int32_t nseg, float* segm_out,
+                             float* segm_max, float* segm_expsum, void* stream) {
+  const char* fn = "mla_verify_attn";
+  mla::AttnArgs a;
+  bool fp8 = false;
+  const mla_status_t st = attn_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype,
+                                    kv_scale, sm_scale, row_lens, page_table, pt_width, q_start,
+                                    N, R, H, W, max_qlen, nseg, a, fp8);
+  if (st != MLA_OK) return st;
+  if (!segm_out || !segm_max || !segm_expsum)
+    return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+  if (!aligned16(segm_out))
+    return fail(MLA_ERR_INVALID, "%s: segm_out must be 16-byte aligned", fn);
   a.segm_out = segm_out; a.segm_max = segm_max; a.segm_expsum = segm_expsum;
   return hip_status(mla::launch_attn(a, fp8, (hipStream_t)stream), "mla_verify_attn launch");
+}
+
+mla_status_t mla_verify_attn_shard(const void* q, const void* kv, int64_t num_blocks,
+                                   int32_t block_size, int32_t page_size,
+                                   mla_kv_dtype_t kv_dtype, float kv_scale, float sm_scale,
+                                   const int32_t* row_lens, const int32_t* page_table,
+                                   int32_t pt_width, const int32_t* q_start, int32_t N,
+                                   int32_t R, int32_t H, int32_t W, int32_t max_qlen,
+                                   void* shard_out, float* shard_lse, void* stream) {
+  const char* fn = "mla_verify_attn_shard";
+  mla::AttnArgs a;
+  bool fp8 = false;
+  const mla_status_t st = attn_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype,
+                                    kv_scale, sm_scale, row_lens, page_table, pt_width, q_start,
+                                    N, R, H, W, max_qlen, 1, a, fp8);
+  if (st != MLA_OK) return st;
+  if (!shard_out || !shard_lse) return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+  if (!aligned16(shard_out))
+    return fail(MLA_ERR_INVALID, "%s: shard_out must be 16-byte aligned", fn);
+  a.shard_out = static_cast<uint16_t*>(shard_out); a.shard_lse = shard_lse;
+  return hip_status(mla::launch_attn(a, fp8, (hipStream_t)stream),
+                    "mla_verify_attn_shard launch");
 }
 
 mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
@@ -192,6 +243,24 @@ mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
   a.shard_out = static_cast<uint16_t*>(shard_out); a.shard_lse = shard_lse;
   a.out = static_cast<uint16_t*>(out); a.lse = lse;
   return hip_status(mla::launch_merge(a, (hipStream_t)stream), "mla_lse_merge launch");
+}
+
+mla_status_t mla_shard_merge(const void* shard_out, const float* shard_lse, int32_t R,
+                             int32_t H, int32_t W, void* out, float* lse, void* stream) {
+  if (R < 1 || H < 1 || W < 1)
+    return fail(MLA_ERR_INVALID, "mla_shard_merge: R, H, W must be >= 1 (got %d, %d, %d)", R, H,
+                W);
+  if (W > mla::kShardMergeMaxW)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_shard_merge: W %d > %d", W, mla::kShardMergeMaxW);
+  if (!shard_out || !shard_lse || !out || !lse)
+    return fail(MLA_ERR_INVALID, "mla_shard_merge: null tensor argument");
+  if (!aligned16(shard_out) || !aligned16(out))
+    return fail(MLA_ERR_INVALID, "mla_shard_merge: shard_out and out must be 16-byte aligned");
+  mla::ShardMergeArgs a{};
+  a.shard_out = static_cast<const uint16_t*>(shard_out); a.shard_lse = shard_lse;
+  a.R = R; a.H = H; a.W = W;
+  a.out = static_cast<uint16_t*>(out); a.lse = lse;
+  return hip_status(mla::launch_shard_merge(a, (hipStream_t)stream), "mla_shard_merge launch");
 }
 
 }  // extern "C"

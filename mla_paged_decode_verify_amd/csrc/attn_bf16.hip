@@ -47,22 +47,25 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   const unsigned char* zero = zero_row();
   const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
 
-  // ---- Q first (it needs only the request's rows), through the second tile
-  // buffer: free until the first step's barrier, after which the next tile's
-  // loads target it
-  issue_q_tile(a, u, buf1, wave, lane, zero);
+  // ---- the group's length and, for a first segment, its first sub-pages:
+  // two loads in flight together, before any bulk data
+  int32_t vpg = 0;                          // SLICE: pages of tiles 64q .. 64q + 63
+  if constexpr (SLICE) {
+    if (u.s == 0) vpg = first_slice_pages(a, pt_row, wave, lane);
+  }
   decode_tail(a, u);
   const int lo = u.lo, hi = u.hi;
-  if (lo >= hi) {                           // segment inactive for the whole group:
-    MLA_WAIT_VMCNT(0);                      // let the Q loads land before the LDS is released
+  if (lo >= hi) {                           // segment inactive for the whole group
+    store_empty(a, u, wave, lane);
     return;
   }
 
-  // ---- first tile
-  int32_t vpg = 0;                          // SLICE: pages of tiles 64q .. 64q + 63
+  // ---- Q (through the second tile buffer: free until the first step's
+  // barrier, after which the next tile's loads target it), then the first tile
+  issue_q_tile(a, u, buf1, wave, lane, zero);
   Bf16Pages pg;
   if constexpr (SLICE) {
-    vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
+    if (u.s != 0) vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
     const SliceSrc v0 = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, 0), lo + 16 * wave, hi);
 #pragma unroll
     for (int j = 0; j < 18; ++j) issue_slice(v0, zero, buf0, wave, lane, j);

@@ -47,6 +47,7 @@ constexpr int kOTiles = kVDim / 2 / 32;    // 8 output tiles of 32 latent dims p
 constexpr int kTokBytesBf16 = kHeadDim * 2;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;       // log2 units
+constexpr float kLn2 = 0.693147180559945309f;
 
 // Slot permutation of the 16-byte chunks of latent row r.
 __device__ __forceinline__ int lat_swz(int r) { return 0; }
@@ -231,6 +232,18 @@ __device__ inline void decode_tail(const AttnArgs& a, WorkUnit& u) {
   u.lo = u.s * span;
   u.hi = min(u.lo + span, Lg);
 }
+// Sub-pages of the first 64 tiles of a group for one wave (lane j: the
+// slice 64 j + 16 w .. +15), read before the group's length is known: the
+// index is clamped to the table row instead of the segment end. A slice that
+// starts before the segment end lies in one sub-page, whose entry is the same
+// either way; the entries of later slices are never used.
+__device__ __forceinline__ int32_t first_slice_pages(const AttnArgs& a, const int32_t* pt_row,
+                                                     int wave, int lane) {
+  const int64_t tok = min((int64_t)kTile * lane + 16 * wave,
+                          ((int64_t)a.pt_width << a.page_shift) - 1);
+  return pt_row[tok >> a.page_shift];
+}
+
 __device__ inline WorkUnit decode_unit(const AttnArgs& a, int b) {
   WorkUnit u = decode_head(a, b);
   if (u.valid) decode_tail(a, u);
@@ -498,10 +511,34 @@ __device__ __forceinline__ void compute_tile(const unsigned char* __restrict__ t
   }
 }
 
+// Two fp32 values rounded (RNE) to bf16 and packed, the first in the low half.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const __bf16 x = (__bf16)lo, y = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// A unit whose group holds no token on its shard: in the one-segment form
+// its rows still get their (empty) shard results, o_r = 0 and lse_r = -inf;
+// the split form writes nothing (the merge skips segments without tokens).
+__device__ inline void store_empty(const AttnArgs& a, const WorkUnit& u, int wave, int lane) {
+  if (a.shard_out == nullptr) return;
+  const int64_t base = ((int64_t)u.r * a.R + u.qs) * a.H;
+  for (int k = wave; k < kAttnRows && u.m0 + k < u.M; k += 4) {
+    const int64_t e = base + u.m0 + k;
+    *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
+    if (lane == 0) a.shard_lse[e] = kNegInf;
+  }
+}
+
 // End of the segment: add the partner wave's row sums and write the partials
 // (maximum, sum and O relative to the maximum). O goes through LDS (`stage`:
 // this row group's 32 rows, a tile buffer no longer read) so that the global
 // stores write whole rows, 1 KB per instruction, instead of 16-byte pieces.
+// One-segment form (a.shard_out set): the segment merge of a single segment
+// is the normalisation, so the row's output O / sum goes out as bf16 with its
+// natural-log LSE ln2 (max + log2 sum), computed in the same operations and
+// order as the merge kernel would from the partials (same bits).
 constexpr int kStageRow = 4 * kVDim + 16;   // padded row of 512 fp32
 static_assert(32 * kStageRow <= kBufBytes, "a row group's O fits a tile buffer");
 __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit& u,
@@ -522,13 +559,50 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
   // move O and l from the reference exponent to the true maximum
   float fix = 1.f;
   if (st.m_true != kNegInf) fix = __builtin_amdgcn_exp2f(st.m_ref - st.m_true);
+  const bool one_seg = a.shard_out != nullptr;   // uniform
+  const float E = L * fix;
+  const bool live = st.m_true != kNegInf && E > 0.f;
   if (row_ok && c == 0 && h == 0) {
-    const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow) * a.nseg + u.s;
-    a.segm_max[e] = st.m_true;
-    a.segm_expsum[e] = L * fix;
+    if (one_seg) {
+      a.shard_lse[((int64_t)u.r * a.R + u.qs) * a.H + mrow] =
+          live ? kLn2 * (st.m_true + __log2f(E)) : kNegInf;
+    } else {
+      const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow) * a.nseg + u.s;
+      a.segm_max[e] = st.m_true;
+      a.segm_expsum[e] = E;
+    }
   }
   const float vs = fix * a.v_scale;
   float* sp = reinterpret_cast<float*>(stage + n32 * kStageRow) + 256 * c + 4 * h;
+  if (one_seg) {
+    const float inv = live ? 1.f / E : 0.f;
+#pragma unroll
+    for (int t = 0; t < kOTiles; ++t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {st.o[t][4 * q], st.o[t][4 * q + 1], st.o[t][4 * q + 2],
+                         st.o[t][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(sp + 32 * t + 8 * q) = (v * vs) * inv;
+      }
+    }
+    __syncthreads();
+    // wave (g, c) stores rows 16c .. 16c + 15 of its row group: one 1 KB
+    // row of bf16 per instruction, 8 dims per lane
+    const int row0 = u.m0 + 32 * g + 16 * c;
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      if (row0 + k >= u.M) break;
+      const int64_t e = ((int64_t)u.r * a.R + u.qs) * a.H + row0 + k;
+      const float* src = reinterpret_cast<const float*>(stage + (16 * c + k) * kStageRow) + 8 * lane;
+      const float4 x = reinterpret_cast<const float4*>(src)[0];
+      const float4 y = reinterpret_cast<const float4*>(src)[1];
+      uint4 w;
+      w.x = pack2_bf16(x.x, x.y); w.y = pack2_bf16(x.z, x.w);
+      w.z = pack2_bf16(y.x, y.y); w.w = pack2_bf16(y.z, y.w);
+      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = w;
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < kOTiles; ++t) {
 #pragma unroll

@@ -141,22 +141,28 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   const unsigned char* zero = zero_row();
   const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
 
-  // ---- Q first (it needs only the request's rows), staged in the tile buffer
-  issue_q_tile(a, u, buf, wave, lane, zero);
+  // ---- the group's length and, for a first segment, its first sub-pages:
+  // two loads in flight together, before any bulk data
+  int32_t vpg = 0;                          // SLICE: sub-pages of tiles 64q .. 64q + 63
+  if constexpr (SLICE) {
+    if (u.s == 0) vpg = first_slice_pages(a, pt_row, wave, lane);
+  }
   decode_tail(a, u);
   const int lo = u.lo, hi = u.hi;
-  if (lo >= hi) {                           // segment inactive for the whole group:
-    MLA_WAIT_VMCNT(0);                      // let the Q loads land before the LDS is released
+  if (lo >= hi) {                           // segment inactive for the whole group
+    store_empty(a, u, wave, lane);
     return;
   }
   const int ntiles = (hi - lo + kTile - 1) / kTile;
 
-  int32_t vpg = 0;                          // SLICE: sub-pages of tiles 64q .. 64q + 63
+  // ---- Q, staged in the tile buffer
+  issue_q_tile(a, u, buf, wave, lane, zero);
+
   auto issue_tile = [&](int t) {
     unsigned char* st = stage + (t & 1) * kF8Tile;
     const int tb = lo + t * kTile;
     if constexpr (SLICE) {
-      if ((t & 63) == 0) vpg = f8_slice_pages(a, pt_row, tb, hi, wave, lane);
+      if ((t & 63) == 0 && (t != 0 || u.s != 0)) vpg = f8_slice_pages(a, pt_row, tb, hi, wave, lane);
       const int32_t sp = __builtin_amdgcn_readlane(vpg, t & 63);
       F8Slice v;
       const bool ok = sp >= 0 && sp < a.num_subpages;

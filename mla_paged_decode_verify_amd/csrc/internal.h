@@ -45,6 +45,10 @@ struct AttnArgs {
   float* segm_out;
   float* segm_max;
   float* segm_expsum;
+  // One-segment form (segm_* unused, nseg = 1): each row's shard output,
+  // normalised and rounded to bf16, and its natural-log LSE.
+  uint16_t* shard_out;       // [W, R, H, 512] bf16 bits, or null
+  float* shard_lse;          // [W, R, H]
 };
 
 struct MergeArgs {
@@ -60,10 +64,22 @@ struct MergeArgs {
   float* lse;
 };
 
+struct ShardMergeArgs {
+  const uint16_t* shard_out;  // [W, R, H, 512] bf16 bits
+  const float* shard_lse;     // [W, R, H]
+  int32_t R, H, W;
+  uint16_t* out;
+  float* lse;
+};
+
+// Largest W the shard merge takes (its per-wave LDS area).
+constexpr int kShardMergeMaxW = 1024;
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 
 // Rows of one attention workgroup (two groups of 32 rows).
 constexpr int kAttnRows = 64;

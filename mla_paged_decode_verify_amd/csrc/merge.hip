@@ -84,12 +84,16 @@ __device__ inline int active_segments(int Lg, int L, int nseg, int page_size) {
   return min(nact, nseg);
 }
 
-__device__ inline void store_out(const MergeArgs& a, int64_t pair, int lane, const float (&v)[8],
-                                 float lse) {
+__device__ inline void store_out8(uint16_t* out, float* lse, int64_t pair, int lane,
+                                  const float (&v)[8], float l) {
   const uint4 w = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
                              pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
-  *reinterpret_cast<uint4*>(a.out + pair * kVDim + 8 * lane) = w;
-  if (lane == 0) a.lse[pair] = lse;
+  *reinterpret_cast<uint4*>(out + pair * kVDim + 8 * lane) = w;
+  if (lane == 0) lse[pair] = l;
+}
+__device__ inline void store_out(const MergeArgs& a, int64_t pair, int lane, const float (&v)[8],
+                                 float lse) {
+  store_out8(a.out, a.lse, pair, lane, v, lse);
 }
 
 __device__ inline void store_shard(const MergeArgs& a, int r, int rho, int h, int lane,
@@ -291,7 +295,78 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
   store_out(a, pair, lane, res, lse_out);
 }
 
+// Shard merge alone, from per-shard bf16 outputs and natural-log LSEs: one
+// wave per (row, head) pair, each lane owning 8 latent dims. The weights are
+// formed exactly as in merge_kernel (largest LSE G, exp(lse_r - G), wave sum,
+// normalised), and the outputs are accumulated shard by shard in order, so
+// both kernels give the same bits for the same per-shard results.
+__global__ void __launch_bounds__(64 * kMergeWaves) shard_merge_kernel(ShardMergeArgs a) {
+  __shared__ float wsh[kMergeWaves][kShardMergeMaxW];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * kMergeWaves + wave;
+  if (pair >= (int64_t)a.R * a.H) return;
+  const int W = a.W;
+  const int64_t rs = (int64_t)a.R * a.H;    // shard stride, in pairs
+  float* sw = wsh[wave];
+
+  float gm = kNegInf;
+  for (int r = lane; r < W; r += 64) {
+    const float l = a.shard_lse[r * rs + pair];
+    sw[r] = l;
+    gm = fmaxf(gm, l);
+  }
+  const float G = wave_max(gm);
+  float lse_out = kNegInf;
+  if (G != kNegInf) {
+    float part = 0.f;
+    for (int r = lane; r < W; r += 64) {
+      const float wr = sw[r] == kNegInf ? 0.f : __expf(sw[r] - G);
+      sw[r] = wr;
+      part += wr;
+    }
+    const float total = wave_sum(part);
+    lse_out = G + __logf(total);
+    const float inv = 1.f / total;
+    for (int r = lane; r < W; r += 64) sw[r] *= inv;
+  } else {
+    for (int r = lane; r < W; r += 64) sw[r] = 0.f;
+  }
+  wave_lds_sync();
+
+  float res[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) res[k] = 0.f;
+  const uint16_t* src = a.shard_out + pair * kVDim + 8 * lane;
+  for (int r0 = 0; r0 < W; r0 += 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (r0 + j < W) v[j] = *reinterpret_cast<const uint4*>(src + (r0 + j) * rs * kVDim);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (r0 + j >= W) break;
+      const float wr = sw[r0 + j];
+      const uint32_t u32[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        res[2 * k] += wr * __uint_as_float(u32[k] << 16);
+        res[2 * k + 1] += wr * __uint_as_float(u32[k] & 0xFFFF0000u);
+      }
+    }
+  }
+  store_out8(a.out, a.lse, pair, lane, res, lse_out);
+}
+
 }  // namespace
+
+hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s) {
+  const int64_t pairs = (int64_t)a.R * a.H;
+  if (pairs <= 0) return hipSuccess;
+  shard_merge_kernel<<<(unsigned)((pairs + kMergeWaves - 1) / kMergeWaves), 64 * kMergeWaves, 0,
+                       s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.R * a.H;

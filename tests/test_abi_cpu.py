@@ -27,7 +27,7 @@ def test_header_declares_the_abi():
     names = _declared_functions()
     assert names == sorted(["mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes",
                             "mla_verify_plan", "mla_verify_attn", "mla_lse_merge",
-                            "mla_last_error"])
+                            "mla_verify_attn_shard", "mla_shard_merge", "mla_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -129,3 +129,47 @@ def test_python_binding_refuses_host_tensors():
     with pytest.raises(TypeError):
         mla.mla_verify_plan(torch.zeros(1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                             1, 1, torch.zeros(1, 1, dtype=torch.int32), 1, 16, 16)
+
+
+def _attn_shard(**over):
+    a = dict(q=FAKE, kv=FAKE, num_blocks=8, block_size=16, page_size=16, kv_dtype=0,
+             kv_scale=1.0, sm_scale=0.04, row_lens=FAKE, page_table=FAKE, pt_width=4,
+             q_start=FAKE, N=1, R=1, H=16, W=1, max_qlen=1, shard_out=FAKE, shard_lse=FAKE,
+             stream=None)
+    a.update(over)
+    return _lib.lib.mla_verify_attn_shard(*a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=0), _lib.MLA_ERR_INVALID),
+    (dict(page_size=8), _lib.MLA_ERR_INVALID),
+    (dict(kv_dtype=7), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(sm_scale=-0.04), _lib.MLA_ERR_INVALID),
+    (dict(kv_dtype=1, kv_scale=0.0), _lib.MLA_ERR_INVALID),
+    (dict(shard_out=None), _lib.MLA_ERR_INVALID),
+    (dict(shard_lse=None), _lib.MLA_ERR_INVALID),
+    (dict(shard_out=FAKE + 8), _lib.MLA_ERR_INVALID),
+    (dict(max_qlen=0), _lib.MLA_ERR_INVALID),
+])
+def test_attn_shard_rejects_bad_arguments(over, code):
+    assert _attn_shard(**over) == code
+    assert "mla_verify_attn_shard" in mla.mla_last_error()
+
+
+def _shard_merge(**over):
+    a = dict(shard_out=FAKE, shard_lse=FAKE, R=1, H=1, W=1, out=FAKE, lse=FAKE, stream=None)
+    a.update(over)
+    return _lib.lib.mla_shard_merge(*a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(R=0), _lib.MLA_ERR_INVALID),
+    (dict(W=0), _lib.MLA_ERR_INVALID),
+    (dict(W=1025), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(out=None), _lib.MLA_ERR_INVALID),
+    (dict(shard_lse=None), _lib.MLA_ERR_INVALID),
+    (dict(shard_out=FAKE + 2), _lib.MLA_ERR_INVALID),
+])
+def test_shard_merge_rejects_bad_arguments(over, code):
+    assert _shard_merge(**over) == code
+    assert "mla_shard_merge" in mla.mla_last_error()

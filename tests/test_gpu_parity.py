@@ -349,3 +349,84 @@ def test_two_stage_verify_matches_one_stage_and_oracle(W, I):
     one = run_gpu(inp)
     assert out_excess(got_out, one["out"], "bf16") <= 1.0
     assert max_err(got_lse, one["lse"]) <= TOL_LSE
+
+
+# ------------------------------------------ one-segment (shard output) path ---
+
+def _run_shards(inp, poison=True):
+    """plan -> mla_verify_attn_shard -> mla_shard_merge, into buffers filled
+    with NaN first, so that any element left unwritten fails."""
+    dev = wl.to_device(inp)
+    W, R, H = inp["W"], inp["R"], inp["H"]
+    fill = float("nan") if poison else 0.0
+    so = torch.full((W, R, H, 512), fill, dtype=torch.bfloat16, device="cuda")
+    sl = torch.full((W, R, H), fill, dtype=torch.float32, device="cuda")
+    out = torch.full((R, H, 512), fill, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((R, H), fill, dtype=torch.float32, device="cuda")
+    res = mla.mla_verify_forward_shards(dev, shards=(so, sl), out=out, lse=lse)
+    torch.cuda.synchronize()
+    return {k: res[k].cpu() for k in ("shard_out", "shard_lse", "out", "lse")}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_one_segment_path(name):
+    """The one-segment path (segment merge folded into the attention kernel,
+    then the shard merge alone) against the oracle's per-shard and final
+    results, and bit for bit against plan -> attn (nseg 1) -> lse_merge."""
+    spec = dict(SMALL[name])
+    inp = wl.make_workload(spec, seed=1)
+    say(f"one-segment case {name} S={inp['seq_lens'].tolist()} Q={inp['qlens'].tolist()}")
+    got = _run_shards(inp)
+    ref_plan = oracle_plan(inp)
+    so, sl, _ = oracle_shard_results(inp, ref_plan, 1)
+    g_so = got["shard_out"].float().numpy().astype(np.float64)
+    g_sl = got["shard_lse"].numpy().astype(np.float64)
+    assert not np.any(np.isnan(g_so)) and not np.any(np.isnan(g_sl))
+    assert out_excess(g_so, so, inp["kv_dtype"]) <= 1.0
+    assert max_err(g_sl, sl) <= TOL_LSE
+    out_ref, lse_ref = orc.verify_reference(inp)
+    g_out = got["out"].float().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g_out)) and not np.any(np.isnan(got["lse"].numpy()))
+    assert out_excess(g_out, out_ref, inp["kv_dtype"]) <= 1.0
+    assert max_err(got["lse"].numpy(), lse_ref) <= TOL_LSE
+    # the split path with one segment computes the same per-shard and final bits
+    split = run_gpu(inp, nseg=1, want_shards=True)
+    assert np.array_equal(g_so, split["shard_out"])
+    assert np.array_equal(g_sl, split["shard_lse"])
+    assert np.array_equal(g_out, split["out"])
+    assert np.array_equal(got["lse"].numpy().astype(np.float64), split["lse"])
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "verify_dcp8"])
+def test_one_segment_path_named_workload(name):
+    """The one-segment path on the full-size workloads that run with one
+    segment: out / lse against the oracle on sampled requests."""
+    inp = named_workload(name)
+    got = _run_shards(inp)
+    g = {"out": got["out"].float().numpy().astype(np.float64),
+         "lse": got["lse"].numpy().astype(np.float64)}
+    assert np.all(np.isfinite(g["out"])) and np.all(np.isfinite(g["lse"]))
+    reqs = sample_requests(inp, {"tiny_decode": 2, "verify_dcp8": 32}[name])
+    eo, el, ex, *_ = compare_requests(inp, g, reqs)
+    say(f"one-segment {name}: max|dout|={eo:.3e} max|dlse|={el:.3e} excess={ex:.3f}")
+    assert ex <= 1.0
+    assert el <= TOL_LSE
+
+
+def test_shard_merge_alone_matches_oracle_merge():
+    """mla_shard_merge on given per-shard results (some shards empty: -inf)
+    against the oracle's LSE merge of the same bf16 values, and an all-empty
+    pair giving out 0, lse -inf."""
+    rng = np.random.default_rng(5)
+    W, R, H = 5, 3, 4
+    so = torch.tensor(rng.standard_normal((W, R, H, 512)), dtype=torch.bfloat16)
+    sl = torch.tensor(rng.normal(3.0, 2.0, (W, R, H)), dtype=torch.float32)
+    sl[1, 0, :] = -float("inf")
+    sl[:, 2, 3] = -float("inf")
+    out, lse = mla.mla_shard_merge(so.cuda(), sl.cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.lse_merge(so.double().numpy(), sl.double().numpy())
+    got_o = out.float().cpu().numpy()
+    assert out_excess(got_o, o_ref, "bf16") <= 1.0
+    assert max_err(lse.cpu().numpy(), l_ref) <= 1e-5
+    assert np.all(got_o[2, 3] == 0.0) and lse[2, 3].item() == -float("inf")

@@ -61,16 +61,20 @@ def parse():
     return ap.parse_args()
 
 
-ATTN_SOURCES = ["attn_common.h", "attn_bf16.hip", "attn_fp8.hip", "internal.h"]
+# sources of the attention kernel that runs a workload, by its KV dtype
+ATTN_SOURCES = {"bf16": ["attn_common.h", "attn_bf16.hip", "internal.h"],
+                "fp8": ["attn_common.h", "attn_fp8.hip", "internal.h"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_verify_dcp8_traffic.txt")
 
 
-def attn_source_hash():
-    """sha256 over the attention kernel sources (to tell whether stored
-    counter readings still describe the current kernel)."""
+def attn_source_hash(workload="verify_dcp8"):
+    """sha256 over the sources of the attention kernel that runs `workload`
+    (to tell whether stored counter readings still describe that kernel)."""
     import hashlib
+    import workloads as wl
+    kind = "bf16" if wl.CONFIGS[workload]["kv_dtype"] == "bf16" else "fp8"
     h = hashlib.sha256()
-    for name in ATTN_SOURCES:
+    for name in ATTN_SOURCES[kind]:
         with open(os.path.join(ROOT, "mla_paged_decode_verify_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -87,7 +91,7 @@ def stored_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("workload") != workload or kv.get("source_sha256") != attn_source_hash():
+    if kv.get("workload") != workload or kv.get("source_sha256") != attn_source_hash(workload):
         return None
     try:
         return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
@@ -108,7 +112,7 @@ def stored_mfma_flops(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.split("(")[0].strip()] = v.split()[0] if v.split() else ""
-    if kv.get("source_sha256") != attn_source_hash():
+    if kv.get("workload") != workload or kv.get("source_sha256") != attn_source_hash(workload):
         return None
     try:
         return float(kv["executed_mfma_flops_per_launch"])

@@ -308,6 +308,53 @@ __global__ void __launch_bounds__(64 * kMergeWaves) shard_merge_kernel(ShardMerg
   if (pair >= (int64_t)a.R * a.H) return;
   const int W = a.W;
   const int64_t rs = (int64_t)a.R * a.H;    // shard stride, in pairs
+  const uint16_t* src = a.shard_out + pair * kVDim + 8 * lane;
+  float res[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) res[k] = 0.f;
+
+  if (W <= 8) {
+    // Up to 8 shards: every load goes out at once, and each lane forms all the
+    // weights itself. The sum of the weights follows the butterfly order of
+    // wave_sum over lanes 0..W-1 (zeros elsewhere), so the bits are those of
+    // the general path.
+    float l[8];
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) l[j] = j < W ? a.shard_lse[j * rs + pair] : kNegInf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < W) v[j] = *reinterpret_cast<const uint4*>(src + j * rs * kVDim);
+    float G = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) G = fmaxf(G, l[j]);
+    float lse_out = kNegInf;
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = 0.f;
+    if (G != kNegInf) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = l[j] == kNegInf ? 0.f : __expf(l[j] - G);
+      const float total = ((w[0] + w[4]) + (w[2] + w[6])) + ((w[1] + w[5]) + (w[3] + w[7]));
+      lse_out = G + __logf(total);
+      const float inv = 1.f / total;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] *= inv;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= W) break;
+      const uint32_t u32[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        res[2 * k] += w[j] * __uint_as_float(u32[k] << 16);
+        res[2 * k + 1] += w[j] * __uint_as_float(u32[k] & 0xFFFF0000u);
+      }
+    }
+    store_out8(a.out, a.lse, pair, lane, res, lse_out);
+    return;
+  }
+
   float* sw = wsh[wave];
 
   float gm = kNegInf;
@@ -334,10 +381,6 @@ __global__ void __launch_bounds__(64 * kMergeWaves) shard_merge_kernel(ShardMerg
   }
   wave_lds_sync();
 
-  float res[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) res[k] = 0.f;
-  const uint16_t* src = a.shard_out + pair * kVDim + 8 * lane;
   for (int r0 = 0; r0 < W; r0 += 8) {
     uint4 v[8];
 #pragma unroll

@@ -37,30 +37,42 @@ __device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W, 
   return w > 0 ? (int32_t)shard_count(w, r, W, I) : 0;
 }
 
+// Sub-page ids staged in LDS per request: entry k of every table row of the
+// request is the same value (sub-page k of the request's blocks), so it is
+// computed once, from the block ids the validity check has already read.
+constexpr int kPlanLdsPages = 4096;
+
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
+  __shared__ int32_t pages_lds[kPlanLdsPages];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int qs = a.q_start[i], qe = a.q_start[i + 1];
   const int S = a.seq_lens[i];
+  const int per = a.block_size / a.page_size;   // sub-pages per block
 
   // ---- request checks (uniform), then the block ids it uses (all threads)
   uint32_t bits = 0;
   if (qs < 0 || qe > a.R || qe - qs < 1 || S < qe - qs) bits |= MLA_PLAN_ERR_QLEN;
   int64_t nb = 0;
+  int64_t npages = 0;                        // sub-pages of the longest local sequence
   if (S >= 0) {
     const int64_t local_max = shard_count(S, 0, a.W, a.I);   // shard 0 holds the most
     if (local_max > a.max_kv_seq_len) bits |= MLA_PLAN_ERR_BOUND;
     nb = (local_max + a.block_size - 1) / a.block_size;
+    npages = (local_max + a.page_size - 1) / a.page_size;
     if (nb > a.max_blocks) {
       bits |= MLA_PLAN_ERR_BLOCKS;
       nb = 0;
     }
   }
   const int32_t* bt = a.block_table + (int64_t)i * a.max_blocks;
+  const bool staged = npages <= kPlanLdsPages;  // uniform
   int bad = 0;
   for (int64_t b = tid; b < nb; b += kPlanThreads) {
     const int32_t id = bt[b];
     bad |= (id < 0 || (int64_t)id >= a.num_blocks);
+    if (staged)
+      for (int j = 0; j < per && b * per + j < npages; ++j) pages_lds[b * per + j] = id * per + j;
   }
   if (__syncthreads_or(bad)) bits |= MLA_PLAN_ERR_BLOCKS;
   if (tid == 0 && a.err_flag != nullptr) {
@@ -83,9 +95,24 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   }
 
   // ---- sub-page table cells (r, rho, k): page k holds local tokens
-  // [kP, kP + P); cells past the row's last page are -1
-  const int per = a.block_size / a.page_size;
-  const int64_t cells = (int64_t)a.W * nrows * a.pt_width;
+  // [kP, (k+1)P), i.e. sub-page k % per of block k / per; cells past the
+  // row's last page are -1
+  const int64_t rows = (int64_t)a.W * nrows;
+  if (staged && rows * a.pt_width < 0x7FFFFFFF) {
+    // 32-bit indices; the page ids come from LDS
+    const int ptw = a.pt_width;
+    const int cells = (int)rows * ptw;
+    for (int idx = tid; idx < cells; idx += kPlanThreads) {
+      const int row = idx / ptw;
+      const int k = idx - row * ptw;
+      const int r = row / nrows, rho = r0 + (row - r * nrows);
+      const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
+      const int pages = (L + a.page_size - 1) / a.page_size;
+      a.page_table[((int64_t)r * a.R + rho) * ptw + k] = k < pages ? pages_lds[k] : -1;
+    }
+    return;
+  }
+  const int64_t cells = rows * a.pt_width;
   for (int64_t idx = tid; idx < cells; idx += kPlanThreads) {
     const int k = (int)(idx % a.pt_width);
     const int64_t row = idx / a.pt_width;
@@ -93,10 +120,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
     const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
     const int pages = (L + a.page_size - 1) / a.page_size;
     int32_t v = -1;
-    if (k < pages) {
-      const int64_t first = (int64_t)k * a.page_size;  // first local token of page k
-      v = bt[first / a.block_size] * per + (int32_t)((first % a.block_size) / a.page_size);
-    }
+    if (k < pages) v = bt[k / per] * per + k % per;
     a.page_table[((int64_t)r * a.R + rho) * a.pt_width + k] = v;
   }
 }

@@ -413,15 +413,17 @@ def test_one_segment_path_named_workload(name):
     assert el <= TOL_LSE
 
 
-def test_shard_merge_alone_matches_oracle_merge():
+@pytest.mark.parametrize("W", [1, 5, 8, 12, 70])
+def test_shard_merge_alone_matches_oracle_merge(W):
     """mla_shard_merge on given per-shard results (some shards empty: -inf)
     against the oracle's LSE merge of the same bf16 values, and an all-empty
-    pair giving out 0, lse -inf."""
-    rng = np.random.default_rng(5)
-    W, R, H = 5, 3, 4
+    pair giving out 0, lse -inf (W <= 8 and the general path, which holds
+    shards past 64 in a second pass)."""
+    rng = np.random.default_rng(5 + W)
+    R, H = 3, 4
     so = torch.tensor(rng.standard_normal((W, R, H, 512)), dtype=torch.bfloat16)
     sl = torch.tensor(rng.normal(3.0, 2.0, (W, R, H)), dtype=torch.float32)
-    sl[1, 0, :] = -float("inf")
+    sl[min(1, W - 1), 0, :] = -float("inf")
     sl[:, 2, 3] = -float("inf")
     out, lse = mla.mla_shard_merge(so.cuda(), sl.cuda())
     torch.cuda.synchronize()

@@ -77,6 +77,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   int mrow, hi_row;
   bool row_ok;
   lane_row(a, u, g, lane, mrow, hi_row, row_ok);
+  const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
   WaveState st;
   state_init(st);
   MLA_WAIT_VMCNT(0);
@@ -112,7 +113,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
         if (more && (j & 1) == 0) issue_slice(v, zero, nxt, wave, lane, j >> 1);
       }
     };
-    compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
+    if (idle)
+      idle_tile(issue);
+    else
+      compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
   };
   int kt = 0;
   for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {

@@ -531,6 +531,19 @@ __device__ inline void store_empty(const AttnArgs& a, const WorkUnit& u, int wav
   }
 }
 
+// A tile for a wave whose row group holds no row of the block (the last
+// block of a request whose Q_i * H is not a multiple of 64 may fill only its
+// first row group): the wave issues its share of the next tile's loads and
+// meets compute_tile's two barriers, and leaves the LDS and the matrix cores
+// to the other row group.
+template <class Issue>
+__device__ __forceinline__ void idle_tile(Issue&& issue) {
+#pragma unroll
+  for (int k = 0; k < kQSteps; ++k) issue(k);
+  lds_barrier();                            // compute_tile: tile maxima published
+  lds_barrier();                            // compute_tile: P fragments published
+}
+
 // End of the segment: add the partner wave's row sums and write the partials
 // (maximum, sum and O relative to the maximum). O goes through LDS (`stage`:
 // this row group's 32 rows, a tile buffer no longer read) so that the global

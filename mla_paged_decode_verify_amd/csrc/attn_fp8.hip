@@ -185,6 +185,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   int mrow, hi_row;
   bool row_ok;
   lane_row(a, u, g, lane, mrow, hi_row, row_ok);
+  const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
   WaveState st;
   state_init(st);
   MLA_WAIT_VMCNT(0);
@@ -197,8 +198,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   if (ntiles > 2) issue_tile(2);
 
   for (int k = 0; k < ntiles; ++k) {
-    compute_tile(buf, &px, qf, st, lo + k * kTile, hi_row, a.qk_scale_log2, g, c, lane,
-                 [](int) {});
+    if (idle)
+      idle_tile([](int) {});
+    else
+      compute_tile(buf, &px, qf, st, lo + k * kTile, hi_row, a.qk_scale_log2, g, c, lane,
+                   [](int) {});
     if (k + 1 < ntiles) {
       // tile k + 1 has landed (this wave's later loads: tile k + 2's nine)
       if (k + 2 < ntiles) MLA_WAIT_VMCNT(kF8Loads); else MLA_WAIT_VMCNT(0);

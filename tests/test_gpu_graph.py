@@ -127,3 +127,61 @@ def test_graph_static_bound_replays_new_lengths():
         got = out.float().cpu().numpy().astype(np.float64)
         assert out_excess(got, out_ref, "bf16") <= 1.0
         assert max_err(lse.cpu().numpy().astype(np.float64), lse_ref) <= TOL_LSE
+
+
+def test_graph_one_segment_route_replays_new_lengths():
+    """The one-segment route (plan -> attn_shard -> shard_merge) captured
+    once; before each replay the requests' lengths change in place, down to
+    S_i = Q_i, which leaves most of the 8 shards without a token (their
+    units write o_r = 0, lse_r = -inf). Every replay equals an eager run of
+    the split route on the new lengths bit for bit, with outputs poisoned
+    before each replay."""
+    spec = small_spec(N=5, W=8, qlen=2, seq_range=(100, 900), nseg=1)
+    inp = wl.make_workload(spec, seed=12)
+    dev = wl.to_device(inp)
+    first = mla.mla_verify_forward_shards(dev)
+    torch.cuda.synchronize()
+    plan_bufs = {k: torch.empty_like(first["plan"][k])
+                 for k in ("row_lens", "page_table", "qo_indptr")}
+    plan_bufs["err_flag"] = torch.zeros_like(first["plan"]["err_flag"])
+    shards = (torch.empty_like(first["shard_out"]), torch.empty_like(first["shard_lse"]))
+    out, lse = torch.empty_like(first["out"]), torch.empty_like(first["lse"])
+
+    def step():
+        plan = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
+                                   dev["block_table"], dev["num_blocks"], dev["block_size"],
+                                   dev["max_kv_seq_len"], **plan_bufs)
+        mla.mla_verify_forward_shards(dev, plan=plan, shards=shards, out=out, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(6)
+    S0, Q = inp["seq_lens"].copy(), inp["qlens"]
+    for rep in range(4):
+        S = np.array([int(rng.integers(q, s + 1)) for q, s in zip(Q, S0)], dtype=np.int64)
+        if rep == 1:
+            S[:3] = Q[:3]                         # 2 tokens over 8 shards
+        say(f"  replay {rep}: S={S.tolist()}")
+        dev["seq_lens"].copy_(torch.from_numpy(S.astype(np.int32)).to("cuda"))
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        for b in shards:
+            b.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = mla.mla_verify_forward(dev, nseg=1, want_shards=True)
+        torch.cuda.synchronize()
+        assert int(plan_bufs["err_flag"].item()) == 0
+        assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
+        assert torch.equal(shards[0], ref["shard_out"])
+        assert torch.equal(shards[1], ref["shard_lse"])

@@ -25,17 +25,23 @@ namespace {
 
 constexpr int kPlanThreads = 256;
 
-// Positions of a window of w that shard r holds (w >= 0).
-__device__ __forceinline__ int64_t shard_count(int64_t w, int r, int W, int I) {
-  const int64_t cyc = (int64_t)I * W;
-  const int64_t c = w / cyc, rem = w - c * cyc;
-  return c * I + min(max(rem - (int64_t)r * I, (int64_t)0), (int64_t)I);
+// Positions of a window of w (0 <= w < 2^31) that shard r holds. The host
+// guarantees I * W <= 2^30, so 32-bit unsigned arithmetic is exact: the
+// count is at most w, r * I < 2^30 and the remainder is below I * W.
+__device__ __forceinline__ int32_t shard_count(int32_t w, int r, int W, int I) {
+  const uint32_t cyc = (uint32_t)I * (uint32_t)W;
+  const uint32_t c = (uint32_t)w / cyc;
+  const int32_t rem = (int32_t)((uint32_t)w - c * cyc);
+  return (int32_t)(c * (uint32_t)I) + min(max(rem - r * I, 0), I);
 }
 // Rows of shard r, row t of a request with window base S - Q (w = S - Q + 1 + t).
 __device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W, int I) {
   const int w = S - Q + 1 + t;       // window length of row t
-  return w > 0 ? (int32_t)shard_count(w, r, W, I) : 0;
+  return w > 0 ? shard_count(w, r, W, I) : 0;
 }
+
+// Row lengths of one request kept in LDS for its table cells.
+constexpr int kPlanLdsRows = 1024;
 
 // Sub-page ids staged in LDS per request: entry k of every table row of the
 // request is the same value (sub-page k of the request's blocks), so it is
@@ -44,6 +50,7 @@ constexpr int kPlanLdsPages = 4096;
 
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   __shared__ int32_t pages_lds[kPlanLdsPages];
+  __shared__ int32_t len_lds[kPlanLdsRows];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int qs = a.q_start[i], qe = a.q_start[i + 1];
@@ -88,26 +95,31 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   const int Q = qe - qs;
   const int nrows = r1 - r0;
   if (nrows <= 0) return;
+  const int64_t rows = (int64_t)a.W * nrows;
+  const bool lens_staged = rows <= kPlanLdsRows;  // uniform
   for (int idx = tid; idx < a.W * nrows; idx += kPlanThreads) {
     const int r = idx / nrows, rho = r0 + idx % nrows;
-    a.row_lens[(int64_t)r * a.R + rho] = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
+    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
+    a.row_lens[(int64_t)r * a.R + rho] = L;
+    if (lens_staged) len_lds[idx] = L;
     if (r == 0 && a.qo_indptr != nullptr) a.qo_indptr[rho] = rho;
   }
+  if (lens_staged) __syncthreads();
 
   // ---- sub-page table cells (r, rho, k): page k holds local tokens
   // [kP, (k+1)P), i.e. sub-page k % per of block k / per; cells past the
   // row's last page are -1
-  const int64_t rows = (int64_t)a.W * nrows;
-  if (staged && rows * a.pt_width < 0x7FFFFFFF) {
-    // 32-bit indices; the page ids come from LDS
-    const int ptw = a.pt_width;
-    const int cells = (int)rows * ptw;
-    for (int idx = tid; idx < cells; idx += kPlanThreads) {
-      const int row = idx / ptw;
-      const int k = idx - row * ptw;
-      const int r = row / nrows, rho = r0 + (row - r * nrows);
-      const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
-      const int pages = (L + a.page_size - 1) / a.page_size;
+  if (staged && lens_staged && rows * a.pt_width < 0x7FFFFFFF) {
+    // 32-bit indices; row lengths and page ids come from LDS
+    const uint32_t ptw = (uint32_t)a.pt_width;
+    const uint32_t cells = (uint32_t)rows * ptw;
+    const int shift = __builtin_ctz((unsigned)a.page_size);
+    for (uint32_t idx = tid; idx < cells; idx += kPlanThreads) {
+      const uint32_t row = idx / ptw;
+      const int k = (int)(idx - row * ptw);
+      const int r = (int)row / nrows, rho = r0 + ((int)row - r * nrows);
+      const int32_t L = len_lds[row];
+      const int pages = (L + a.page_size - 1) >> shift;
       a.page_table[((int64_t)r * a.R + rho) * ptw + k] = k < pages ? pages_lds[k] : -1;
     }
     return;

@@ -432,3 +432,31 @@ def test_shard_merge_alone_matches_oracle_merge(W):
     assert out_excess(got_o, o_ref, "bf16") <= 1.0
     assert max_err(lse.cpu().numpy(), l_ref) <= 1e-5
     assert np.all(got_o[2, 3] == 0.0) and lse[2, 3].item() == -float("inf")
+
+
+@pytest.mark.parametrize("case", ["many_subpages", "many_shard_rows"])
+def test_plan_paths_past_the_lds_staging(case):
+    """The plan kernel keeps a request's sub-page ids (up to 4096) and its
+    (shard, row) lengths (up to 1024) in LDS; larger requests take the path
+    that reads the block table per cell. Both paths against the oracle, bit
+    for bit, in one batch with a small request that stays on the LDS path."""
+    rng = np.random.default_rng(21)
+    if case == "many_subpages":        # 70000 tokens in 16-token sub-pages: 4375 > 4096
+        W, B, S, Q = 1, 16, [70000, 300], [3, 2]
+    else:                              # 64 shards x 17 rows = 1088 > 1024
+        W, B, S, Q = 64, 16, [5000, 900], [17, 1]
+    local = [-(-s // W) for s in S]
+    nblk = [-(-l // B) for l in local]
+    max_blocks = max(nblk)
+    num_blocks = sum(nblk) + 7
+    ids = rng.permutation(num_blocks)
+    bt = np.full((2, max_blocks), -1, dtype=np.int32)
+    bt[0, :nblk[0]] = ids[:nblk[0]]
+    bt[1, :nblk[1]] = ids[nblk[0]:nblk[0] + nblk[1]]
+    max_kv = max(local)
+    p = _plan_raw(S, Q, W, bt, num_blocks, B, max_kv)
+    q_start = np.concatenate([[0], np.cumsum(Q)]).astype(np.int64)
+    ref = orc.plan(np.asarray(S), q_start, W, bt, B, max_kv)
+    assert int(p["err_flag"].item()) == 0
+    assert np.array_equal(p["row_lens"].cpu().numpy(), ref["row_lens"])
+    assert np.array_equal(p["page_table"].cpu().numpy(), ref["page_table"])

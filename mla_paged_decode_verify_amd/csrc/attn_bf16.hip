@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   // two loads in flight together, before any bulk data
   int32_t vpg = 0;                          // SLICE: pages of tiles 64q .. 64q + 63
   if constexpr (SLICE) {
-    if (u.s == 0) vpg = first_slice_pages(a, pt_row, wave, lane);
+    if (u.s == 0 && a.pt_width > 0) vpg = first_slice_pages(a, pt_row, wave, lane);
   }
   decode_tail(a, u);
   const int lo = u.lo, hi = u.hi;

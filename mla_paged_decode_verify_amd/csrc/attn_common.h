@@ -236,7 +236,8 @@ __device__ inline void decode_tail(const AttnArgs& a, WorkUnit& u) {
 // slice 64 j + 16 w .. +15), read before the group's length is known: the
 // index is clamped to the table row instead of the segment end. A slice that
 // starts before the segment end lies in one sub-page, whose entry is the same
-// either way; the entries of later slices are never used.
+// either way; the entries of later slices are never used. Needs a table row
+// of at least one entry (pt_width >= 1).
 __device__ __forceinline__ int32_t first_slice_pages(const AttnArgs& a, const int32_t* pt_row,
                                                      int wave, int lane) {
   const int64_t tok = min((int64_t)kTile * lane + 16 * wave,

@@ -460,3 +460,27 @@ def test_plan_paths_past_the_lds_staging(case):
     assert int(p["err_flag"].item()) == 0
     assert np.array_equal(p["row_lens"].cpu().numpy(), ref["row_lens"])
     assert np.array_equal(p["page_table"].cpu().numpy(), ref["page_table"])
+
+
+def test_empty_page_table_is_safe():
+    """max_kv_seq_len = 0: the plan flags every request (its shard-0 length
+    exceeds the bound) and gives it length 0; the table has width 0 (a null or
+    empty buffer). Both routes then read no table entry and return out 0,
+    lse -inf for every row, with no NaN."""
+    inp = wl.make_workload(small_spec(N=3, W=4, qlen=3, seq_range=(20, 90), block_size=16),
+                           seed=2)
+    dev = wl.to_device(inp)
+    dev["max_kv_seq_len"] = 0
+    for route in ("split", "shards"):
+        if route == "split":
+            res = mla.mla_verify_forward(dev, nseg=1)
+        else:
+            res = mla.mla_verify_forward_shards(dev)
+        torch.cuda.synchronize()
+        assert res["plan"]["pt_width"] == 0
+        assert int(res["plan"]["err_flag"].item()) & mla.MLA_PLAN_ERR_BOUND
+        assert int(res["plan"]["row_lens"].abs().sum().item()) == 0
+        out = res["out"].float().cpu()
+        lse = res["lse"].cpu()
+        assert torch.all(out == 0), route
+        assert torch.all(torch.isneginf(lse)), route

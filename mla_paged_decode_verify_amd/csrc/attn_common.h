@@ -554,6 +554,7 @@ __device__ __forceinline__ void idle_tile(Issue&& issue) {
 // natural-log LSE ln2 (max + log2 sum), computed in the same operations and
 // order as the merge kernel would from the partials (same bits).
 constexpr int kStageRow = 4 * kVDim + 16;   // padded row of 512 fp32
+constexpr int kStageRowBf16 = 2 * kVDim + 16;  // padded row of 512 bf16
 static_assert(32 * kStageRow <= kBufBytes, "a row group's O fits a tile buffer");
 __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit& u,
                                                const WaveState& st, RowExchange& rx,
@@ -589,14 +590,17 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
   const float vs = fix * a.v_scale;
   float* sp = reinterpret_cast<float*>(stage + n32 * kStageRow) + 256 * c + 4 * h;
   if (one_seg) {
+    // rows staged already rounded to bf16 (half the LDS traffic of fp32)
     const float inv = live ? 1.f / E : 0.f;
+    unsigned char* sb = stage + n32 * kStageRowBf16 + 2 * (256 * c + 4 * h);
 #pragma unroll
     for (int t = 0; t < kOTiles; ++t) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {st.o[t][4 * q], st.o[t][4 * q + 1], st.o[t][4 * q + 2],
-                         st.o[t][4 * q + 3]};
-        *reinterpret_cast<f32x4*>(sp + 32 * t + 8 * q) = (v * vs) * inv;
+        const f32x4 v = (f32x4{st.o[t][4 * q], st.o[t][4 * q + 1], st.o[t][4 * q + 2],
+                               st.o[t][4 * q + 3]} * vs) * inv;
+        *reinterpret_cast<uint2*>(sb + 2 * (32 * t + 8 * q)) =
+            make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
       }
     }
     __syncthreads();
@@ -607,13 +611,8 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
     for (int k = 0; k < 16; ++k) {
       if (row0 + k >= u.M) break;
       const int64_t e = ((int64_t)u.r * a.R + u.qs) * a.H + row0 + k;
-      const float* src = reinterpret_cast<const float*>(stage + (16 * c + k) * kStageRow) + 8 * lane;
-      const float4 x = reinterpret_cast<const float4*>(src)[0];
-      const float4 y = reinterpret_cast<const float4*>(src)[1];
-      uint4 w;
-      w.x = pack2_bf16(x.x, x.y); w.y = pack2_bf16(x.z, x.w);
-      w.z = pack2_bf16(y.x, y.y); w.w = pack2_bf16(y.z, y.w);
-      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = w;
+      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) =
+          *reinterpret_cast<const uint4*>(stage + (16 * c + k) * kStageRowBf16 + 16 * lane);
     }
     return;
   }

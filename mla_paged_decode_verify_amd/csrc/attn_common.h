@@ -606,14 +606,17 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
     __syncthreads();
     // wave (g, c) stores rows 16c .. 16c + 15 of its row group: one 1 KB
     // row of bf16 per instruction, 8 dims per lane
+    // (all 16 LDS reads first, then the stores: one LDS round trip, not 16)
     const int row0 = u.m0 + 32 * g + 16 * c;
-#pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-      if (row0 + k >= u.M) break;
-      const int64_t e = ((int64_t)u.r * a.R + u.qs) * a.H + row0 + k;
-      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) =
-          *reinterpret_cast<const uint4*>(stage + (16 * c + k) * kStageRowBf16 + 16 * lane);
-    }
+    uint4 rows[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      rows[k] = *reinterpret_cast<const uint4*>(stage + (16 * c + k) * kStageRowBf16 + 16 * lane);
+    const int64_t e0 = ((int64_t)u.r * a.R + u.qs) * a.H + row0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (row0 + k < u.M)
+        *reinterpret_cast<uint4*>(a.shard_out + (e0 + k) * kVDim + 8 * lane) = rows[k];
     return;
   }
 #pragma unroll
@@ -625,18 +628,27 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
     }
   }
   __syncthreads();
-  // wave (g, c) stores rows 16c .. 16c + 15 of its row group, half a row a go
+  // wave (g, c) stores rows 16c .. 16c + 15 of its row group, half a row a
+  // go, eight rows' LDS reads in flight before their stores
   const int row0 = u.m0 + 32 * g + 16 * c;
-#pragma unroll 4
-  for (int k = 0; k < 16; ++k) {
-    if (row0 + k >= u.M) break;
-    const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + row0 + k) * a.nseg + u.s;
-    const unsigned char* src = stage + (16 * c + k) * kStageRow + 16 * lane;
-    float* dst = a.segm_out + e * kVDim + 4 * lane;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      *reinterpret_cast<float4*>(dst + 256 * hh) =
-          *reinterpret_cast<const float4*>(src + 1024 * hh);
+  for (int k0 = 0; k0 < 16; k0 += 8) {
+    float4 v[8][2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const unsigned char* src = stage + (16 * c + k0 + k) * kStageRow + 16 * lane;
+      v[k][0] = *reinterpret_cast<const float4*>(src);
+      v[k][1] = *reinterpret_cast<const float4*>(src + 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (row0 + k0 + k < u.M) {
+        const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + row0 + k0 + k) * a.nseg + u.s;
+        float* dst = a.segm_out + e * kVDim + 4 * lane;
+        *reinterpret_cast<float4*>(dst) = v[k][0];
+        *reinterpret_cast<float4*>(dst + 256) = v[k][1];
+      }
+    }
   }
 }
 

@@ -91,7 +91,11 @@ int32_t mla_pt_width(int32_t max_kv_seq_len, int32_t page_size);
 /*
  * Bytes of the three split-K partial buffers for W shards, R rows, H heads and
  * nseg segments: segm_out (W*R*H*nseg*512 floats) + segm_max and segm_expsum
- * (W*R*H*nseg floats each). Returns 0 on bad input. Host only.
+ * (W*R*H*nseg floats each). These are the per-segment output, base-2 maximum
+ * and exp2 sum that the segment merge folds ([V51705] Implementation
+ * breakdown item 4 and the `merge_mla_segments_triton` snippet, whose
+ * segm_output / segm_max / segm_expsum arguments carry one 512-wide output and
+ * two scalars per row, head and segment). Returns 0 on bad input. Host only.
  */
 size_t mla_verify_workspace_bytes(int32_t W, int32_t R, int32_t H, int32_t nseg);
 
@@ -142,6 +146,56 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
                              void* stream);
 
 /*
+ * Two-stage verify plan: the metadata of the SGLang decomposition of the same
+ * verify result ([S34432] Implementation breakdown items 2-3 and the
+ * `_forward_verify_dcp` snippet: a per-row local KV length and a per-row 2-D
+ * token table for the committed prefix, read row by row, plus a dense causal
+ * window over the verify tokens computed by one source, merged by LSE). Built
+ * once per forward on the device; the attention and merge calls below then
+ * run it unchanged:
+ *   stage 1  every shard attends over its part of the request's committed
+ *            prefix [0, S_i - Q_i): row_lens[r][rho] = positions of the
+ *            prefix that shard r holds (the same for every row of a request),
+ *            page_table[r][rho] = their sub-pages, exactly as mla_verify_plan
+ *            builds them for a window of S_i - Q_i. Run mla_verify_attn with
+ *            row_lens rows 0..W-1, page_table, q_start, nseg 1.
+ *   stage 2  one extra source attends over the dense causal window of the
+ *            request's Q_i verify tokens: row t sees verify tokens 0..t, so
+ *            row_lens[W][rho] = t + 1 and window_table[rho][k] = q_start[i] + k
+ *            for k <= t, else -1: the row of verify token k in a caller's
+ *            window buffer [R, 576] that holds the verify tokens' cache
+ *            entries request-major (as on the page). Run mla_verify_attn with
+ *            kv = that buffer viewed as [1, R, 1, 576] (num_blocks R,
+ *            block_size 1, page_size 1), row_lens row W, window_table as
+ *            page_table (pt_width = max_qlen), q_start, W = 1, nseg 1.
+ *   merge    mla_lse_merge over the W + 1 sources (row_lens [W+1, R], nseg 1).
+ *
+ *   N, seq_lens, q_start, R, W, interleave, block_table, max_blocks,
+ *   num_blocks, block_size, page_size, max_kv_seq_len, pt_width: as for
+ *              mla_verify_plan (same checks, same error codes)
+ *   max_qlen   >= 1, the width of window_table; a request with Q_i above it
+ *              gets MLA_PLAN_ERR_QLEN (and length 0, table -1 everywhere)
+ * Outputs (device):
+ *   row_lens     [W+1, R] int32 (stage-1 rows 0..W-1, stage-2 row W)
+ *   page_table   [W, R, pt_width] int32
+ *   window_table [R, max_qlen] int32
+ *   err_flag     as for mla_verify_plan (sticky; may be NULL). An empty
+ *                committed prefix (S_i = Q_i) is no error: its stage-1
+ *                lengths are 0.
+ */
+mla_status_t mla_verify_two_stage_plan(int32_t N, const int32_t* seq_lens,
+                                       const int32_t* q_start, int32_t R,
+                                       int32_t W, int32_t interleave,
+                                       const int32_t* block_table,
+                                       int32_t max_blocks, int64_t num_blocks,
+                                       int32_t block_size, int32_t page_size,
+                                       int32_t max_kv_seq_len, int32_t pt_width,
+                                       int32_t max_qlen, int32_t* row_lens,
+                                       int32_t* page_table,
+                                       int32_t* window_table,
+                                       uint32_t* err_flag, void* stream);
+
+/*
  * Split-K segmented attention partials for every (shard, row, head, segment)
  * ([V51705] Implementation breakdown item 4 and the merge snippet).
  *
@@ -153,7 +207,11 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
  *              product sm_scale * kv_scale * log2(e) must be a positive
  *              finite fp32 value, else MLA_ERR_INVALID
  *   row_lens, page_table, pt_width, page_size: from mla_verify_plan
- *   q_start    [N+1] as given to the plan; max_qlen >= every Q_i
+ *   q_start    [N+1] as given to the plan
+ *   max_qlen   the largest Q_i: it sizes the grid (ceil(max_qlen*H/64) row
+ *              blocks per request). A smaller value is still correct (the
+ *              extra row blocks of a longer request are taken in turn by the
+ *              same workgroups), only slower.
  *   nseg       segments per (request, shard) group. Partition (a reading of
  *              the pages' tiles_per_segment = ceil(len/(nseg*TILE))): with Lg
  *              the group's longest row (its last), T = ceil(Lg/(nseg*P)) and
@@ -165,7 +223,10 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens,
  *   segm_out[e*512 + d] sum of 2^(score2 - segm_max[e]) * v[d]  (unnormalised)
  * Only segments with s*T*P < Lg are written; entries of other segments are
  * left untouched (mla_lse_merge does not read them). A row with no token in
- * a written segment gets (-inf, 0, 0).
+ * a written segment gets maximum -inf and sum 0 (its segm_out entry is then
+ * 0 or left untouched; the merge gives such a segment weight 0 and never
+ * reads it). Local tokens past pt_width * page_size are never read (the plan
+ * keeps every length within the table).
  */
 mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
                              int32_t block_size, int32_t page_size,
@@ -212,14 +273,15 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv,
  * breakdown item 4; [S34432] review item 4 for the natural-log convention).
  * Per shard r, over its active segments (s*T*P < that row's length):
  *   M = max m2_s, E = sum e_s 2^(m2_s - M), o_r = sum O_s 2^(m2_s - M) / E,
- *   lse_r = ln2 * (M + log2 E)   (natural log; -inf and o_r = 0 if none),
- * o_r rounded to bf16 as a shard would send it. Then across shards:
+ *   lse_r = ln2 * (M + log2 E)   (natural log; -inf and o_r = 0 if none).
+ * Then across shards, with o_r kept in fp32 (every shard is on this device):
  *   lse = ln sum_r exp(lse_r), out = sum_r exp(lse_r - lse) * o_r  -> bf16.
- * Never produces NaN from empty shards or segments.
+ * Never produces NaN from empty shards or segments. A row's length is read
+ * as at most its group's last row's (the segments mla_verify_attn wrote).
  *
  *   segm_*       from mla_verify_attn with the same R, H, W, nseg
  *   row_lens, q_start, N, page_size: as given to mla_verify_attn
- *   shard_out    [W, R, H, 512] bf16, may be NULL   (per-shard o_r)
+ *   shard_out    [W, R, H, 512] bf16, may be NULL   (per-shard o_r, rounded)
  *   shard_lse    [W, R, H] fp32, may be NULL        (per-shard lse_r)
  *   out          [R, H, 512] bf16
  *   lse          [R, H] fp32, natural log, unpadded in heads

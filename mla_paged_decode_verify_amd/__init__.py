@@ -312,76 +312,102 @@ def mla_verify_forward_shards(dev, *, plan=None, shards=None, out=None, lse=None
     return {"plan": plan, "shard_out": so, "shard_lse": sl, "out": o, "lse": l}
 
 
-def mla_verify_two_stage(dev, k_window, *, stream=None):
-    """The SGLang decomposition of the same verify result, from the same native
-    calls ([S34432] implementation item 3, the _forward_verify_dcp snippet):
+def mla_verify_two_stage_plan(seq_lens, q_start, R, W, block_table, num_blocks, block_size,
+                              max_kv_seq_len, max_qlen, *, page_size=None, pt_width=None,
+                              interleave=1, row_lens=None, page_table=None, window_table=None,
+                              err_flag=None, stream=None):
+    """Metadata of the two-stage verify (see mla_verify_two_stage): row lengths
+    [W+1, R] (stage-1 committed prefix per shard in rows 0..W-1, stage-2 window
+    t + 1 in row W), the stage-1 sub-page table [W, R, pt_width], the stage-2
+    window token table [R, max_qlen] and the sticky device error word."""
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(q_start, torch.int32, "q_start")
+    _dev(block_table, torch.int32, "block_table")
+    N = seq_lens.shape[0]
+    if q_start.shape != (N + 1,):
+        raise ValueError("q_start must have N+1 entries")
+    if block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("block_table must be [N, max_blocks]")
+    if page_size is None:
+        page_size = mla_subpage_size(block_size)
+    if pt_width is None:
+        pt_width = mla_pt_width(max_kv_seq_len, page_size)
+    dev = seq_lens.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    if row_lens is None:
+        row_lens = torch.empty((W + 1, R), **i32)
+    if page_table is None:
+        page_table = torch.empty((W, R, max(pt_width, 0)), **i32)
+    if window_table is None:
+        window_table = torch.empty((R, max_qlen), **i32)
+    if err_flag is None:
+        err_flag = torch.zeros((1,), **i32)  # sticky: starts clear
+    for t, n in ((row_lens, "row_lens"), (page_table, "page_table"),
+                 (window_table, "window_table"), (err_flag, "err_flag")):
+        _dev(t, torch.int32, n)
+    if tuple(row_lens.shape) != (W + 1, R) or tuple(page_table.shape) != (W, R, pt_width) \
+            or tuple(window_table.shape) != (R, max_qlen):
+        raise ValueError("row_lens / page_table / window_table shape mismatch")
+    _check(_lib.lib.mla_verify_two_stage_plan(
+        N, _ptr(seq_lens), _ptr(q_start), int(R), int(W), interleave, _ptr(block_table),
+        block_table.shape[1], int(num_blocks), block_size, page_size, max_kv_seq_len,
+        pt_width, int(max_qlen), _ptr(row_lens), _ptr(page_table), _ptr(window_table),
+        _ptr(err_flag), _stream(stream)))
+    return {"row_lens": row_lens, "page_table": page_table, "window_table": window_table,
+            "err_flag": err_flag, "page_size": page_size, "pt_width": pt_width, "R": R}
+
+
+def mla_verify_two_stage(dev, k_window, *, plan=None, stream=None):
+    """The SGLang decomposition of the same verify result, from native calls
+    ([S34432] implementation items 2-3, the _forward_verify_dcp snippet):
 
       stage 1 -- every shard attends over its part of the request's committed
                  prefix [0, S_i - Q_i) (every verify row sees the same prefix);
-      stage 2 -- one shard attends over the dense causal window of the
+      stage 2 -- one extra source attends over the dense causal window of the
                  request's Q_i verify tokens (row t sees verify tokens 0..t),
                  read from ``k_window`` [R, 576] bf16 (row rho = the entry of
                  verify token rho, request-major, as the snippet lays it out);
       merge   -- natural-log LSE merge over the W stage-1 shards and stage 2.
 
-    Both stages treat every verify row as a one-row request (q_start =
-    0..R), so one merge sees a consistent grouping; stage 2's pool is
-    ``k_window`` viewed as R blocks of one token. nseg is 1 (the two stages
-    have different sub-page sizes, and with one segment the partition does
-    not depend on them). A row whose request has no committed token has an
-    empty stage 1 (the plan flags it in a private error word). ``dev`` is a
-    dict as for mla_verify_forward. Returns (out, lse)."""
+    mla_verify_two_stage_plan builds both stages' lengths and tables on the
+    device; stage 2's pool is ``k_window`` viewed as R blocks of one token.
+    ``dev`` is a dict as for mla_verify_forward. Returns (out, lse, err_flag):
+    the plan's sticky error word (int32 device tensor, 0 when every request
+    is valid)."""
     q, kv = dev["q"], dev["kv"]
     R, H, _ = q.shape
     W = dev["W"]
-    I = dev.get("interleave", 1)
-    d = q.device
-    i32 = dict(dtype=torch.int32, device=d)
     _dev(k_window, torch.bfloat16, "k_window")
     if tuple(k_window.shape) != (R, HEAD_DIM):
         raise ValueError("k_window must be [R, 576]")
-    q_start = dev["q_start"].long()
-    N = q_start.shape[0] - 1
-    qlens = q_start[1:] - q_start[:-1]
-    req = torch.repeat_interleave(torch.arange(N, device=d), qlens)      # request of each row
-    t = torch.arange(R, device=d) - q_start[:-1][req]                    # row index in request
-    rows = torch.arange(R + 1, **i32)
-    # ---- stage 1: committed prefix, sharded
-    S1 = (dev["seq_lens"].long()[req] - qlens[req]).to(torch.int32).contiguous()
-    bt1 = dev["block_table"][req].contiguous()
-    row_lens = torch.empty((W + 1, R), **i32)
-    flag = torch.zeros((1,), **i32)
-    p1 = mla_verify_plan(S1, rows, R, W, bt1, dev["num_blocks"], dev["block_size"],
-                         dev["max_kv_seq_len"], interleave=I, row_lens=row_lens[:W],
-                         err_flag=flag, stream=stream)
-    parts = (torch.empty((W + 1, R, H, 1, V_DIM), dtype=torch.float32, device=d),
-             torch.empty((W + 1, R, H, 1), dtype=torch.float32, device=d),
-             torch.empty((W + 1, R, H, 1), dtype=torch.float32, device=d))
-    mla_verify_attn(q, kv, p1["row_lens"], p1["page_table"], rows, page_size=p1["page_size"],
-                    max_qlen=1, nseg=1, sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+    qmax = int(dev["max_qlen"])
+    if plan is None:
+        plan = mla_verify_two_stage_plan(
+            dev["seq_lens"], dev["q_start"], R, W, dev["block_table"], dev["num_blocks"],
+            dev["block_size"], dev["max_kv_seq_len"], qmax,
+            interleave=dev.get("interleave", 1), stream=stream)
+    row_lens = plan["row_lens"]
+    parts = (torch.empty((W + 1, R, H, 1, V_DIM), dtype=torch.float32, device=q.device),
+             torch.empty((W + 1, R, H, 1), dtype=torch.float32, device=q.device),
+             torch.empty((W + 1, R, H, 1), dtype=torch.float32, device=q.device))
+    mla_verify_attn(q, kv, row_lens[:W], plan["page_table"], dev["q_start"],
+                    page_size=plan["page_size"], max_qlen=qmax, nseg=1,
+                    sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
                     segm_out=parts[0][:W], segm_max=parts[1][:W], segm_expsum=parts[2][:W],
                     stream=stream)
-    # ---- stage 2: dense causal window of the verify tokens, one shard
-    qmax = int(dev["max_qlen"])
-    bt2 = q_start[:-1][req].unsqueeze(1) + torch.arange(qmax, device=d).unsqueeze(0)
-    bt2 = torch.where(torch.arange(qmax, device=d).unsqueeze(0) < qlens[req].unsqueeze(1),
-                      bt2, torch.full_like(bt2, -1)).to(torch.int32).contiguous()
-    S2 = (t + 1).to(torch.int32).contiguous()
-    kv2 = k_window.view(1, R, 1, HEAD_DIM)
-    p2 = mla_verify_plan(S2, rows, R, 1, bt2, R, 1, qmax, row_lens=row_lens[W:],
-                         err_flag=flag, stream=stream)
-    mla_verify_attn(q, kv2, p2["row_lens"], p2["page_table"], rows, page_size=1, max_qlen=1,
-                    nseg=1, sm_scale=dev["sm_scale"], segm_out=parts[0][W:],
-                    segm_max=parts[1][W:], segm_expsum=parts[2][W:], stream=stream)
-    # ---- merge over the W + 1 partial sources
-    out, lse, _, _ = mla_lse_merge(*parts, row_lens, rows, page_size=1, H=H, nseg=1,
-                                   stream=stream)
-    return out, lse
+    mla_verify_attn(q, k_window.view(1, R, 1, HEAD_DIM), row_lens[W:],
+                    plan["window_table"].view(1, R, qmax), dev["q_start"], page_size=1,
+                    max_qlen=qmax, nseg=1, sm_scale=dev["sm_scale"],
+                    segm_out=parts[0][W:], segm_max=parts[1][W:], segm_expsum=parts[2][W:],
+                    stream=stream)
+    out, lse, _, _ = mla_lse_merge(*parts, row_lens, dev["q_start"],
+                                   page_size=plan["page_size"], H=H, nseg=1, stream=stream)
+    return out, lse, plan["err_flag"]
 
 
 __all__ = [
     "mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes", "mla_verify_plan",
     "mla_verify_attn", "mla_lse_merge", "mla_verify_attn_shard", "mla_shard_merge",
     "mla_last_error", "mla_verify_forward", "mla_verify_forward_shards",
-    "mla_verify_two_stage", "MlaError", "HEAD_DIM", "V_DIM",
+    "mla_verify_two_stage", "mla_verify_two_stage_plan", "MlaError", "HEAD_DIM", "V_DIM",
 ]

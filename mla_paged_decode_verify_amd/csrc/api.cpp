@@ -70,6 +70,56 @@ size_t mla_verify_workspace_bytes(int32_t W, int32_t R, int32_t H, int32_t nseg)
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both plan entry points; fills everything in `a` but the
+// outputs. `fn` names the entry point in error messages.
+mla_status_t plan_args(const char* fn, int32_t N, const int32_t* seq_lens, const int32_t* q_start,
+                       int32_t R, int32_t W, int32_t interleave, const int32_t* block_table,
+                       int32_t max_blocks, int64_t num_blocks, int32_t block_size,
+                       int32_t page_size, int32_t max_kv_seq_len, int32_t pt_width,
+                       mla::PlanArgs& a) {
+  if (N < 1) return fail(MLA_ERR_INVALID, "%s: N must be >= 1 (got %d)", fn, N);
+  if (R < 1) return fail(MLA_ERR_INVALID, "%s: R must be >= 1 (got %d)", fn, R);
+  if (W < 1) return fail(MLA_ERR_INVALID, "%s: W must be >= 1 (got %d)", fn, W);
+  if (interleave < 1 || (int64_t)interleave * W > (1 << 30))
+    return fail(MLA_ERR_INVALID,
+                "%s: interleave must be >= 1 with interleave * W <= 2^30 (got %d)", fn,
+                interleave);
+  if (block_size <= 0)
+    return fail(MLA_ERR_INVALID, "%s: block_size must be > 0 (got %d)", fn, block_size);
+  if (page_size != subpage_size(block_size))
+    return fail(MLA_ERR_INVALID, "%s: page_size %d != sub-page size %d of block_size %d", fn,
+                page_size, subpage_size(block_size), block_size);
+  if (max_blocks < 1)
+    return fail(MLA_ERR_INVALID, "%s: max_blocks must be >= 1 (got %d)", fn, max_blocks);
+  if (num_blocks < 1) return fail(MLA_ERR_INVALID, "%s: num_blocks must be >= 1", fn);
+  if (num_blocks * (int64_t)(block_size / page_size) > 0x7FFFFFFFLL)
+    return fail(MLA_ERR_INVALID, "%s: too many sub-pages for int32 ids", fn);
+  if (max_kv_seq_len < 0) return fail(MLA_ERR_INVALID, "%s: max_kv_seq_len must be >= 0", fn);
+  if (pt_width < mla_pt_width(max_kv_seq_len, page_size) || pt_width < 0)
+    return fail(MLA_ERR_INVALID, "%s: pt_width %d < ceil(max_kv_seq_len/page_size) = %d", fn,
+                pt_width, mla_pt_width(max_kv_seq_len, page_size));
+  if ((int64_t)W * R * (int64_t)(pt_width > 0 ? pt_width : 1) > (1LL << 40))
+    return fail(MLA_ERR_INVALID, "%s: page table too large", fn);
+  if (!seq_lens || !q_start || !block_table)
+    return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+
+  a = mla::PlanArgs{};
+  a.N = N; a.R = R; a.W = W; a.I = interleave;
+  a.seq_lens = seq_lens; a.q_start = q_start; a.block_table = block_table;
+  a.max_blocks = max_blocks; a.num_blocks = num_blocks;
+  a.block_size = block_size; a.page_size = page_size;
+  a.max_kv_seq_len = max_kv_seq_len; a.pt_width = pt_width;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens, const int32_t* q_start,
                              int32_t R, int32_t W, int32_t interleave,
                              const int32_t* block_table, int32_t max_blocks,
@@ -77,44 +127,48 @@ mla_status_t mla_verify_plan(int32_t N, const int32_t* seq_lens, const int32_t* 
                              int32_t max_kv_seq_len, int32_t pt_width, int32_t* row_lens,
                              int32_t* page_table, int32_t* qo_indptr, uint32_t* err_flag,
                              void* stream) {
-  if (N < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: N must be >= 1 (got %d)", N);
-  if (R < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: R must be >= 1 (got %d)", R);
-  if (W < 1) return fail(MLA_ERR_INVALID, "mla_verify_plan: W must be >= 1 (got %d)", W);
-  if (interleave < 1 || (int64_t)interleave * W > (1 << 30))
-    return fail(MLA_ERR_INVALID,
-                "mla_verify_plan: interleave must be >= 1 with interleave * W <= 2^30 (got %d)",
-                interleave);
-  if (block_size <= 0)
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: block_size must be > 0 (got %d)", block_size);
-  if (page_size != subpage_size(block_size))
-    return fail(MLA_ERR_INVALID,
-                "mla_verify_plan: page_size %d != sub-page size %d of block_size %d",
-                page_size, subpage_size(block_size), block_size);
-  if (max_blocks < 1)
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: max_blocks must be >= 1 (got %d)", max_blocks);
-  if (num_blocks < 1)
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: num_blocks must be >= 1");
-  if (num_blocks * (int64_t)(block_size / page_size) > 0x7FFFFFFFLL)
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: too many sub-pages for int32 ids");
-  if (max_kv_seq_len < 0)
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: max_kv_seq_len must be >= 0");
-  if (pt_width < mla_pt_width(max_kv_seq_len, page_size) || pt_width < 0)
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: pt_width %d < ceil(max_kv_seq_len/page_size) = %d",
-                pt_width, mla_pt_width(max_kv_seq_len, page_size));
-  if ((int64_t)W * R * (int64_t)(pt_width > 0 ? pt_width : 1) > (1LL << 40))
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: page table too large");
-  if (!seq_lens || !q_start || !block_table || !row_lens || (pt_width > 0 && !page_table))
-    return fail(MLA_ERR_INVALID, "mla_verify_plan: null tensor argument");
-
-  mla::PlanArgs a{};
-  a.N = N; a.R = R; a.W = W; a.I = interleave;
-  a.seq_lens = seq_lens; a.q_start = q_start; a.block_table = block_table;
-  a.max_blocks = max_blocks; a.num_blocks = num_blocks;
-  a.block_size = block_size; a.page_size = page_size;
-  a.max_kv_seq_len = max_kv_seq_len; a.pt_width = pt_width;
+  const char* fn = "mla_verify_plan";
+  mla::PlanArgs a;
+  const mla_status_t st = plan_args(fn, N, seq_lens, q_start, R, W, interleave, block_table,
+                                    max_blocks, num_blocks, block_size, page_size,
+                                    max_kv_seq_len, pt_width, a);
+  if (st != MLA_OK) return st;
+  if (!row_lens || (pt_width > 0 && !page_table))
+    return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
   a.row_lens = row_lens; a.page_table = page_table; a.qo_indptr = qo_indptr;
   a.err_flag = err_flag;
   return hip_status(mla::launch_plan(a, (hipStream_t)stream), "mla_verify_plan launch");
+}
+
+mla_status_t mla_verify_two_stage_plan(int32_t N, const int32_t* seq_lens,
+                                       const int32_t* q_start, int32_t R, int32_t W,
+                                       int32_t interleave, const int32_t* block_table,
+                                       int32_t max_blocks, int64_t num_blocks,
+                                       int32_t block_size, int32_t page_size,
+                                       int32_t max_kv_seq_len, int32_t pt_width,
+                                       int32_t max_qlen, int32_t* row_lens,
+                                       int32_t* page_table, int32_t* window_table,
+                                       uint32_t* err_flag, void* stream) {
+  const char* fn = "mla_verify_two_stage_plan";
+  mla::PlanArgs a;
+  const mla_status_t st = plan_args(fn, N, seq_lens, q_start, R, W, interleave, block_table,
+                                    max_blocks, num_blocks, block_size, page_size,
+                                    max_kv_seq_len, pt_width, a);
+  if (st != MLA_OK) return st;
+  if (max_qlen < 1)
+    return fail(MLA_ERR_INVALID, "%s: max_qlen must be >= 1 (got %d)", fn, max_qlen);
+  if ((int64_t)R * max_qlen > (1LL << 40))
+    return fail(MLA_ERR_INVALID, "%s: window table too large", fn);
+  if (!row_lens || (pt_width > 0 && !page_table) || !window_table)
+    return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+  a.row_lens = row_lens; a.page_table = page_table; a.qo_indptr = nullptr;
+  a.err_flag = err_flag;
+  a.prefix_only = 1;
+  a.win_lens = row_lens + (int64_t)W * R;   // the extra source's row of row_lens
+  a.win_table = window_table;
+  a.win_width = max_qlen;
+  return hip_status(mla::launch_plan(a, (hipStream_t)stream),
+                    "mla_verify_two_stage_plan launch");
 }
 
 }  // extern "C"

@@ -197,12 +197,16 @@ struct WorkUnit {
   int qs, Q, M, m0, last;
   int lo, hi;
   bool valid;
+  bool read;                 // the segment starts before the group's end: the merge reads it
 };
 // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8). Request i
 // goes to XCD i % 8, and all its work units (every shard, segment and row
 // block) get consecutive ids on that XCD, so they run side by side: its Q,
 // and each unit's KV across row blocks, come from HBM into that XCD's L2
-// once. The grid covers ceil(N / 8) * 8 requests.
+// once. The grid covers ceil(N / 8) * 8 requests and mblocks row blocks per
+// request; a request with more (row, head) pairs than that (its Q_i above the
+// caller's max_qlen) has them covered too: unit mb also takes row blocks
+// mb + mblocks, mb + 2 mblocks, ... so no output is left unwritten.
 __device__ inline WorkUnit decode_head(const AttnArgs& a, int b) {
   WorkUnit u;
   const int slot = b >> 3;
@@ -223,14 +227,20 @@ __device__ inline WorkUnit decode_head(const AttnArgs& a, int b) {
   u.last = u.qs + u.Q - 1;                  // the group's longest row
   return u;
 }
-// The unit's segment [lo, hi) from the group's longest row (lo >= hi: the
-// segment holds no tokens of this group).
+// The unit's segment [lo, hi) from the group's longest row, its last (lo >=
+// hi: the segment holds no token to read). The partition uses the row's
+// length exactly as the merge does; tokens past the table row are never
+// read (a well-formed plan keeps every length within it), so a segment can be
+// read by the merge (`read`) and still hold no token, and then gets empty
+// partials.
 __device__ inline void decode_tail(const AttnArgs& a, WorkUnit& u) {
-  int Lg = a.row_lens[(int64_t)u.r * a.R + u.last];
-  Lg = min(Lg, a.pt_width * a.page_size);
-  const int span = (Lg + a.nseg * a.page_size - 1) / (a.nseg * a.page_size) * a.page_size;
+  const int Lg = a.row_lens[(int64_t)u.r * a.R + u.last];
+  const int64_t seg_tokens = (int64_t)a.nseg * a.page_size;
+  const int span = (int)((Lg + seg_tokens - 1) / seg_tokens * a.page_size);
   u.lo = u.s * span;
-  u.hi = min(u.lo + span, Lg);
+  u.read = u.lo < Lg;
+  u.hi = (int)min(min((int64_t)u.lo + span, (int64_t)Lg),
+                  (int64_t)a.pt_width * a.page_size);
 }
 // Sub-pages of the first 64 tiles of a group for one wave (lane j: the
 // slice 64 j + 16 w .. +15), read before the group's length is known: the
@@ -519,16 +529,24 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// A unit whose group holds no token on its shard: in the one-segment form
-// its rows still get their (empty) shard results, o_r = 0 and lse_r = -inf;
-// the split form writes nothing (the merge skips segments without tokens).
+// A unit with no token to read, for all its row blocks (see decode_head):
+// in the one-segment form its rows still get their (empty) shard results,
+// o_r = 0 and lse_r = -inf; in the split form a segment the merge reads gets
+// the empty partials (maximum -inf, sum 0: the merge then gives it weight 0
+// and never touches its output), and any other segment nothing.
 __device__ inline void store_empty(const AttnArgs& a, const WorkUnit& u, int wave, int lane) {
-  if (a.shard_out == nullptr) return;
   const int64_t base = ((int64_t)u.r * a.R + u.qs) * a.H;
-  for (int k = wave; k < kAttnRows && u.m0 + k < u.M; k += 4) {
-    const int64_t e = base + u.m0 + k;
-    *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
-    if (lane == 0) a.shard_lse[e] = kNegInf;
+  for (int m0 = u.m0; m0 < u.M; m0 += a.mblocks * kAttnRows) {
+    for (int k = wave; k < kAttnRows && m0 + k < u.M; k += 4) {
+      const int64_t e = base + m0 + k;
+      if (a.shard_out != nullptr) {
+        *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
+        if (lane == 0) a.shard_lse[e] = kNegInf;
+      } else if (u.read && lane == 0) {
+        a.segm_max[e * a.nseg + u.s] = kNegInf;
+        a.segm_expsum[e * a.nseg + u.s] = 0.f;
+      }
+    }
   }
 }
 

@@ -24,6 +24,13 @@ struct PlanArgs {
   int32_t* page_table;
   int32_t* qo_indptr;
   uint32_t* err_flag;
+  // Two-stage form (prefix_only set): every row of a request gets the
+  // committed prefix S_i - Q_i as its window, and the second stage's
+  // lengths [R] and window token table [R, win_width] are written too.
+  int32_t prefix_only;
+  int32_t* win_lens;
+  int32_t* win_table;
+  int32_t win_width;
 };
 
 struct AttnArgs {

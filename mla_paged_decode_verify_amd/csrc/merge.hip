@@ -15,10 +15,11 @@
 // which fixes the segment partition; (3) the partial outputs, each lane owning
 // 8 consecutive latent dims, several segments in flight at once. Statistics go
 // through a small LDS area: per-shard maxima, sums and LSEs, the weight of
-// every segment inside its shard and of every shard in the result. Every
-// per-shard output is rounded to bf16 first, as it would be when a shard sends
-// it to the others. Pairs whose 2 W (nseg + 1) values do not fit the LDS area
-// take a sequential path over shards.
+// every segment inside its shard and of every shard in the result. All shards
+// live on this device, so the per-shard outputs stay in fp32 between the two
+// merges; only the optional shard_out copy is rounded to bf16. Pairs whose
+// 2 W (nseg + 1) values do not fit the LDS area take a sequential path over
+// shards.
 #include "internal.h"
 
 namespace mla {
@@ -55,8 +56,6 @@ __device__ inline int find_request(const int32_t* q_start, int N, int rho, int l
   return lo + cnt - 1;
 }
 
-__device__ inline float bf16_round(float x) { return (float)(__bf16)x; }
-
 __device__ inline uint32_t pack2_bf16(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) |
@@ -74,13 +73,16 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// Segments of a row of length L that hold tokens, in a group whose longest
-// row is Lg: the attention kernel cut the group into segments of `span`
-// tokens.
+// Segments of a row of length L that hold tokens, in a group whose last row
+// has length Lg: the attention kernel cut the group into segments of `span`
+// tokens and wrote the partials of every segment that starts before Lg, for
+// every row of the group. A row is never read past Lg (a well-formed plan has
+// L <= Lg, the last row being the longest), so exactly the segments the
+// attention wrote are read, whatever the row lengths hold.
 __device__ inline int active_segments(int Lg, int L, int nseg, int page_size) {
   const int seg_tokens = nseg * page_size;
-  const int span = (Lg + seg_tokens - 1) / seg_tokens * page_size;
-  const int nact = span > 0 ? (L + span - 1) / span : 0;
+  const int span = (int)(((int64_t)Lg + seg_tokens - 1) / seg_tokens * page_size);
+  const int nact = span > 0 ? (min(L, Lg) + span - 1) / span : 0;
   return min(nact, nseg);
 }
 
@@ -202,14 +204,12 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
     }
     wave_lds_sync();
 
-    // ---- outputs (third round): each lane's 8 dims, shard by shard (bf16
+    // ---- outputs (third round): each lane's 8 dims, shard by shard (fp32
     // per shard); loads are unconditional so that unrolled iterations keep
     // several segments in flight
     const float* src = a.segm_out + pbase * kVDim + 8 * lane;
     const bool want_shard = a.shard_out != nullptr || a.shard_lse != nullptr;
     auto finish_shard = [&](int r, float (&o)[8]) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = bf16_round(o[k]);
       const float wr = sw[r];
 #pragma unroll
       for (int k = 0; k < 8; ++k) res[k] += wr * o[k];
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
       if (E > 0.f) {
         const float inv = 1.f / E;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = bf16_round(o[k] * inv);
+        for (int k = 0; k < 8; ++k) o[k] *= inv;
         lse_r = kLn2 * (M + __log2f(E));
       } else {
 #pragma unroll

@@ -13,6 +13,14 @@
 // Sub-page table: same digest, item 3 -- the physical block table expanded to
 // sub-pages of page_size tokens (block b holds sub-pages b*n .. b*n + n - 1).
 //
+// Two-stage form: SGLang PR #34432 report, Implementation breakdown items 2-3
+// and the _forward_verify_dcp snippet -- stage 1 reads each shard's part of
+// the committed prefix [0, S_i - Q_i) row by row (every row of a request has
+// the same local length and the same table), stage 2 attends over the dense
+// causal window of the Q_i verify tokens, whose entries sit request-major in a
+// separate window buffer (row t of request i sees window rows q_start[i] ..
+// q_start[i] + t).
+//
 // One workgroup per request: it checks the request (the block ids it uses are
 // checked by all threads at once), then writes the request's row lengths and
 // table cells for every shard. Error bits are ORed into the caller's error
@@ -34,9 +42,11 @@ __device__ __forceinline__ int32_t shard_count(int32_t w, int r, int W, int I) {
   const int32_t rem = (int32_t)((uint32_t)w - c * cyc);
   return (int32_t)(c * (uint32_t)I) + min(max(rem - r * I, 0), I);
 }
-// Rows of shard r, row t of a request with window base S - Q (w = S - Q + 1 + t).
-__device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W, int I) {
-  const int w = S - Q + 1 + t;       // window length of row t
+// Rows of shard r, row t of a request with window base S - Q (w = S - Q + 1 + t;
+// the committed prefix w = S - Q in the two-stage form).
+__device__ __forceinline__ int32_t local_len(int S, int Q, int t, int r, int W, int I,
+                                             bool prefix_only) {
+  const int w = prefix_only ? S - Q : S - Q + 1 + t;   // window length of row t
   return w > 0 ? shard_count(w, r, W, I) : 0;
 }
 
@@ -60,6 +70,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   // ---- request checks (uniform), then the block ids it uses (all threads)
   uint32_t bits = 0;
   if (qs < 0 || qe > a.R || qe - qs < 1 || S < qe - qs) bits |= MLA_PLAN_ERR_QLEN;
+  if (a.win_lens != nullptr && qe - qs > a.win_width) bits |= MLA_PLAN_ERR_QLEN;
   int64_t nb = 0;
   int64_t npages = 0;                        // sub-pages of the longest local sequence
   if (S >= 0) {
@@ -99,12 +110,23 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   const bool lens_staged = rows <= kPlanLdsRows;  // uniform
   for (int idx = tid; idx < a.W * nrows; idx += kPlanThreads) {
     const int r = idx / nrows, rho = r0 + idx % nrows;
-    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
+    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I, a.prefix_only);
     a.row_lens[(int64_t)r * a.R + rho] = L;
     if (lens_staged) len_lds[idx] = L;
     if (r == 0 && a.qo_indptr != nullptr) a.qo_indptr[rho] = rho;
   }
   if (lens_staged) __syncthreads();
+
+  // ---- two-stage form: the second stage's window of verify tokens, one
+  // length and one table row per row (row t: window rows qs .. qs + t)
+  if (a.win_lens != nullptr) {
+    for (int idx = tid; idx < nrows * a.win_width; idx += kPlanThreads) {
+      const int rho = r0 + idx / a.win_width, k = idx % a.win_width;
+      const int t = rho - qs;
+      if (k == 0) a.win_lens[rho] = bits ? 0 : t + 1;
+      a.win_table[(int64_t)rho * a.win_width + k] = (!bits && k <= t) ? qs + k : -1;
+    }
+  }
 
   // ---- sub-page table cells (r, rho, k): page k holds local tokens
   // [kP, (k+1)P), i.e. sub-page k % per of block k / per; cells past the
@@ -129,7 +151,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
     const int k = (int)(idx % a.pt_width);
     const int64_t row = idx / a.pt_width;
     const int r = (int)(row / nrows), rho = r0 + (int)(row % nrows);
-    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I);
+    const int32_t L = bits ? 0 : local_len(S, Q, rho - qs, r, a.W, a.I, a.prefix_only);
     const int pages = (L + a.page_size - 1) / a.page_size;
     int32_t v = -1;
     if (k < pages) v = bt[k / per] * per + k % per;

@@ -40,7 +40,7 @@ __all__ = [
     "e5m2_value", "e5m2_table", "decode_e5m2",
     "gather_request_kv", "attention_rows", "shard_local_kv",
     "shard_attention_rows", "segment_partials", "segment_merge", "lse_merge",
-    "two_stage_verify", "verify_reference", "request_rows",
+    "two_stage_plan", "two_stage_verify", "verify_reference", "request_rows",
 ]
 
 
@@ -431,6 +431,44 @@ def lse_merge(outs, lses):
     frac = np.where(has, wts / np.where(has, tot, 1.0), 0.0)
     out = (frac[..., None] * outs).sum(axis=0)
     return out, lse
+
+
+def two_stage_plan(seq_lens, q_start, W, block_table, block_size, max_kv_seq_len,
+                   max_qlen, interleave=1):
+    """Metadata of the two-stage verify, built per forward.
+
+    [S34432] Implementation breakdown items 2-3 and the ``_forward_verify_dcp``
+    snippet: stage 1 gives every verify row its request's committed prefix
+    [0, S - Q) on each shard (a per-row local length and a per-row token table,
+    read row by row); stage 2 gives row t the dense causal window of verify
+    tokens 0..t, whose entries sit request-major in a separate window buffer
+    (request i's verify token k at row q_start[i] + k).
+    Stage-1 lengths are counted one position at a time, like ``row_view``.
+    Returns row_lens [W+1, R] (stage 1 in rows 0..W-1, stage 2 in row W), the
+    stage-1 sub-page table [W, R, width] and window_table [R, max_qlen]
+    (-1 past each row's window).
+    """
+    seq_lens = [int(x) for x in seq_lens]
+    q_start = [int(x) for x in q_start]
+    N = len(seq_lens)
+    R = q_start[N]
+    P = subpage_size(block_size)
+    L = np.zeros((W + 1, R), dtype=np.int64)
+    win = np.full((R, int(max_qlen)), -1, dtype=np.int64)
+    for i in range(N):
+        qs, Q = request_rows(q_start, i)
+        committed = seq_lens[i] - Q
+        owner = shard_of(np.arange(committed, dtype=np.int64), W, interleave)
+        counts = np.bincount(owner, minlength=W)[:W] if committed > 0 else np.zeros(W, np.int64)
+        for t in range(Q):
+            L[:W, qs + t] = counts
+            L[W, qs + t] = t + 1
+            for k in range(t + 1):
+                win[qs + t, k] = qs + k
+    width = -(-int(max_kv_seq_len) // P)
+    pt = subpage_table(L[:W], block_table, q_start, block_size, P, width)
+    return {"page_size": P, "row_lens": L, "page_table": pt, "window_table": win,
+            "pt_width": width}
 
 
 def two_stage_verify(q_rows, K, seq_len: int, qlen: int, W: int,

@@ -11,14 +11,20 @@ import numpy as np
 import oracle as orc
 import workloads as wl
 
-TOL_OUT = {"bf16": 1e-2, "fp8_e4m3": 3e-2, "fp8_e5m2": 3e-2}   # absolute floor on out
-TOL_LSE = 1e-3                                # max-abs on lse
-# The output is bf16 (8 significant bits) and the path rounds to bf16 three
-# times: the softmax weights fed to the PV product, each shard's output as it
-# is handed to the shard merge, and the final output -- each at most 2^-9
-# relative. So |got - ref| <= max(floor, 2^-7 |ref|): for |ref| <= 1.28 this is
-# the plain max-abs floor; above that the bf16 format's own spacing dominates.
-REL_OUT = 2.0 ** -7
+TOL_OUT = {"bf16": 1e-2, "fp8_e4m3": 3e-2, "fp8_e5m2": 3e-2}   # stated max-abs on out
+TOL_LSE = 1e-3                                # stated max-abs on lse
+# Where a bf16 format the method fixes forces a rounding, the stated bound can
+# be out of reach: rounding x to bf16 (round to nearest even, 8 significant
+# bits) errs by up to half the spacing of bf16 numbers at |x|, 2^(e - 8) for
+# |x| in [2^e, 2^(e+1)), i.e. up to 2^-8 |x| (the unit roundoff). The final
+# output is bf16 (half-spacing 2^-6 = 0.0156 > 1e-2 from |x| = 4 on), and on the
+# one-segment route each shard's output is handed to the shard merge as bf16
+# (its error enters the result weighted by the shard's share). Such elements
+# get the forced roundings plus EPS_PRE, the allowance for everything before
+# them (fp32 accumulation and the bf16 softmax weights on the matrix cores):
+# EPS_PRE = 2^-9 is what the stated 1e-2 leaves above the largest final
+# rounding below |x| = 4 (2^-7), so every other element keeps the plain bound.
+EPS_PRE = 2.0 ** -9
 
 
 def say(*a):
@@ -65,43 +71,73 @@ def oracle_plan(inp):
 
 
 def max_err(a, b):
+    """max |a - b|; equal infinities count as 0, NaN as +inf."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    d = np.abs(np.where(both_inf, 0.0, a) - np.where(both_inf, 0.0, b))
+    d = np.where(np.isnan(d), np.inf, d)
     return float(np.max(d)) if d.size else 0.0
 
 
-def out_excess(got, ref, kv_dtype):
-    """max over elements of |got - ref| / max(floor, 2^-7 |ref|); <= 1 passes."""
+def half_ulp_bf16(x):
+    """Largest error of rounding x to bf16 (nearest even): 2^(e-8) for |x| in
+    [2^e, 2^(e+1)); 0 at 0."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 8), 0.0)
+
+
+def out_bound(ref, kv_dtype, shard_ref=None, shard_lse_ref=None, lse_ref=None):
+    """Per-element bound on |out - ref|: the stated max-abs bound, unless the
+    forced bf16 roundings (of ref itself, and with shard_ref given, of every
+    shard's output weighted by its share exp(lse_r - lse)) plus EPS_PRE exceed
+    it."""
+    ref = np.asarray(ref, dtype=np.float64)
+    forced = half_ulp_bf16(ref)
+    if shard_ref is not None:
+        sl = np.asarray(shard_lse_ref, dtype=np.float64)
+        lr = np.asarray(lse_ref, dtype=np.float64)
+        wts = np.where(np.isfinite(sl), np.exp(sl - np.where(np.isfinite(lr), lr, 0.0)), 0.0)
+        forced = forced + np.sum(wts[..., None] * half_ulp_bf16(shard_ref), axis=0)
+    return np.maximum(TOL_OUT[kv_dtype], forced + EPS_PRE)
+
+
+def check_out(got, ref, kv_dtype, what="out", shard_ref=None, shard_lse_ref=None,
+              lse_ref=None):
+    """Assert |got - ref| <= out_bound element by element and print the
+    max-abs error, the max over elements held to the plain stated bound, and
+    how many elements the forced-rounding exception covers."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if not got.size:
-        return 0.0
-    bound = np.maximum(TOL_OUT[kv_dtype], REL_OUT * np.abs(ref))
-    return float(np.max(np.abs(got - ref) / bound))
+        return 0.0, 0
+    bound = out_bound(ref, kv_dtype, shard_ref, shard_lse_ref, lse_ref)
+    d = np.abs(got - ref)
+    d = np.where(np.isnan(d), np.inf, d)
+    tol = TOL_OUT[kv_dtype]
+    exc = bound > tol
+    plain = float(d[~exc].max()) if (~exc).any() else 0.0
+    worst = float(d.max())
+    say(f"  {what}: max|d|={worst:.3e} (elements held to {tol:g}: max {plain:.3e}); "
+        f"{int(exc.sum())} of {d.size} elements past it by forced bf16 rounding"
+        + (f" (max bound {float(bound.max()):.4f}, max|d| there "
+           f"{float(d[exc].max()):.3e})" if exc.any() else ""))
+    bad = d > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of bound; worst "
+                           f"|d|={worst:.4g} at |ref|={float(np.abs(ref.ravel()[np.argmax(d)])):.4g}")
+    return worst, int(exc.sum())
 
 
-def compare_requests(inp, got, requests):
-    """Max errors of out / lse over the given requests vs the oracle."""
+def compare_requests(inp, got, requests, what="out"):
+    """out / lse of the given requests vs the oracle (split route: only the
+    final output's bf16 rounding is forced). Returns (max|dout|, max|dlse|)."""
     ref_out, ref_lse = orc.verify_reference(inp, requests)
     rows = np.concatenate([np.arange(inp["q_start"][i], inp["q_start"][i + 1]) for i in requests])
-    eo = max_err(got["out"][rows], ref_out[rows])
+    eo, _ = check_out(got["out"][rows], ref_out[rows], inp["kv_dtype"], what)
     el = max_err(got["lse"][rows], ref_lse[rows])
-    ex = out_excess(got["out"][rows], ref_out[rows], inp["kv_dtype"])
-    return eo, el, ex, ref_out, ref_lse, rows
-
-
-def sample_requests(inp, k):
-    """The longest, the shortest and k-2 evenly spaced other requests."""
-    N = inp["N"]
-    if N <= k:
-        return list(range(N))
-    S = inp["seq_lens"]
-    pick = {int(np.argmax(S)), int(np.argmin(S))}
-    for i in np.linspace(0, N - 1, k):
-        pick.add(int(i))
-    return sorted(pick)[:max(k, 2)]
+    say(f"  lse: max|d|={el:.3e}")
+    return eo, el
 
 
 def small_spec(**kw):
@@ -111,9 +147,9 @@ def small_spec(**kw):
     return spec
 
 
-def oracle_shard_results(inp, plan, nseg):
-    """Per-shard (out, lse) and the segment partials from the oracle, for every
-    request, using the oracle's own plan."""
+def oracle_shard_results(inp, plan, nseg, want_parts=True):
+    """Per-shard (out, lse) and (want_parts) the segment partials from the
+    oracle, for every request, using the oracle's own plan."""
     q = orc.decode_bf16(inp["q_bits"])
     W, R, H = inp["W"], inp["R"], inp["H"]
     so = np.zeros((W, R, H, 512))
@@ -130,6 +166,7 @@ def oracle_shard_results(inp, plan, nseg):
             Lr = plan["row_lens"][r, qs:qs + Q]
             o, l = orc.shard_attention_rows(q[qs:qs + Q], local, Lr, inp["sm_scale"])
             so[r, qs:qs + Q], sl[r, qs:qs + Q] = o, l
-            parts[(i, r)] = orc.segment_partials(q[qs:qs + Q], local, Lr, nseg,
-                                                 plan["page_size"], inp["sm_scale"])
+            if want_parts:
+                parts[(i, r)] = orc.segment_partials(q[qs:qs + Q], local, Lr, nseg,
+                                                     plan["page_size"], inp["sm_scale"])
     return so, sl, parts

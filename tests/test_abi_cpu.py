@@ -26,8 +26,9 @@ def _declared_functions():
 def test_header_declares_the_abi():
     names = _declared_functions()
     assert names == sorted(["mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes",
-                            "mla_verify_plan", "mla_verify_attn", "mla_lse_merge",
-                            "mla_verify_attn_shard", "mla_shard_merge", "mla_last_error"])
+                            "mla_verify_plan", "mla_verify_two_stage_plan", "mla_verify_attn",
+                            "mla_lse_merge", "mla_verify_attn_shard", "mla_shard_merge",
+                            "mla_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -79,6 +80,30 @@ def _plan(**over):
 def test_plan_rejects_bad_arguments(over, code, msg):
     assert _plan(**over) == code
     assert msg in mla.mla_last_error()
+
+
+def _two_stage_plan(**over):
+    a = dict(N=1, seq_lens=FAKE, q_start=FAKE, R=4, W=2, interleave=1, block_table=FAKE,
+             max_blocks=4, num_blocks=8, block_size=64, page_size=64, max_kv_seq_len=100,
+             pt_width=2, max_qlen=4, row_lens=FAKE, page_table=FAKE, window_table=FAKE,
+             err_flag=None, stream=None)
+    a.update(over)
+    return _lib.lib.mla_verify_two_stage_plan(*a.values())
+
+
+@pytest.mark.parametrize("over,msg", [
+    (dict(interleave=0), "interleave"),
+    (dict(page_size=32), "page_size"),
+    (dict(pt_width=1), "pt_width"),
+    (dict(N=0), "N"),
+    (dict(max_qlen=0), "max_qlen"),
+    (dict(window_table=None), "null"),
+    (dict(row_lens=None), "null"),
+])
+def test_two_stage_plan_rejects_bad_arguments(over, msg):
+    assert _two_stage_plan(**over) == _lib.MLA_ERR_INVALID
+    err = mla.mla_last_error()
+    assert msg in err and "mla_verify_two_stage_plan" in err
 
 
 def _attn(**over):

@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle on cuda:0.
 
 Plans (row lengths, sub-page tables, qo_indptr) must match bit for bit.
-Outputs: |out - ref| <= max(1e-2 (bf16 KV) or 3e-2 (fp8 KV), 2^-7 |ref|) --
-the floor is the stated max-abs bound, the relative term the spacing of the bf16
-output format (see tests/helpers.py) -- and max-abs 1e-3 on the LSE.
+Outputs: max-abs 1e-2 (bf16 KV) or 3e-2 (fp8 KV) per element, except where a
+bf16 format the method fixes forces a larger rounding (the bf16 output at
+|ref| >= 4, and on the one-segment route each shard's bf16 hand-off): there
+the forced roundings plus 2^-9 (see tests/helpers.py); each check prints how
+many elements that covers. LSE: max-abs 1e-3.
 """
 
 import math
@@ -13,9 +15,8 @@ import pytest
 
 import oracle as orc
 import workloads as wl
-from helpers import (TOL_LSE, TOL_OUT, compare_requests, max_err, named_workload,
-                     oracle_plan, oracle_shard_results, out_excess, run_gpu,
-                     sample_requests, say, small_spec)
+from helpers import (TOL_LSE, TOL_OUT, check_out, compare_requests, max_err, named_workload,
+                     oracle_plan, oracle_shard_results, run_gpu, say, small_spec)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,10 +82,11 @@ def test_small_parity_all_stages(name, nseg):
     ref = _check_plan(inp, got)
     so, sl, parts = oracle_shard_results(inp, ref, nseg)
     assert np.all(np.isfinite(got["out"])) and not np.any(np.isnan(got["lse"]))
-    assert out_excess(got["shard_out"], so, inp["kv_dtype"]) <= 1.0
+    check_out(got["shard_out"], so, inp["kv_dtype"], "shard_out")
     assert max_err(got["shard_lse"], sl) <= TOL_LSE
-    # split-K partials on active (row, segment) pairs
+    # split-K partials on active (row, segment) pairs (fp32: the plain bound)
     H, W, R = inp["H"], inp["W"], inp["R"]
+    tol = TOL_OUT[inp["kv_dtype"]]
     gm = got["segm_max"].reshape(W, R, H, nseg)
     ge = got["segm_expsum"].reshape(W, R, H, nseg)
     go = got["segm_out"].reshape(W, R, H, nseg, 512)
@@ -95,11 +97,11 @@ def test_small_parity_all_stages(name, nseg):
                 rho = qs + t
                 assert max_err(gm[r, rho, :, s], m2[t, :, s]) <= 1e-3
                 assert np.allclose(ge[r, rho, :, s], e[t, :, s], rtol=2e-3, atol=0)
-                assert out_excess(go[r, rho, :, s] / ge[r, rho, :, s, None],
-                                  O[t, :, s] / e[t, :, s, None], inp["kv_dtype"]) <= 1.0
+                assert max_err(go[r, rho, :, s] / ge[r, rho, :, s, None],
+                               O[t, :, s] / e[t, :, s, None]) <= tol
     out_ref, lse_ref = orc.verify_reference(inp)
-    say(f"  max|dout|={max_err(got['out'], out_ref):.3e} max|dlse|={max_err(got['lse'], lse_ref):.3e}")
-    assert out_excess(got["out"], out_ref, inp["kv_dtype"]) <= 1.0
+    check_out(got["out"], out_ref, inp["kv_dtype"], "out")
+    say(f"  lse: max|d|={max_err(got['lse'], lse_ref):.3e}")
     assert max_err(got["lse"], lse_ref) <= TOL_LSE
 
 
@@ -232,6 +234,92 @@ def test_output_discriminates_off_by_one_window():
     assert checked >= 6
 
 
+def _window_oracle(q_row, K, w, sm_scale):
+    """Oracle out [H, 512] and lse [H] of one row attending to positions [0, w)."""
+    o, l = orc.attention_rows(q_row[None], K, w, 1, sm_scale)
+    return o[0], l[0]
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "tiny_decode_q4", "verify_dcp8"])
+def test_every_row_discriminates_its_window(name):
+    """On every row of the tiny-decode and verify workloads (and a qlen-4
+    variant of the tiny one), the GPU result is closer to the oracle with the
+    pages' window w = S - Q + 1 + t than to the oracle with w - 1 or w + 1
+    (where w + 1 <= S), in L2 over all heads for both the LSE and the output:
+    at these lengths max-abs 1e-2 alone cannot see a one-token window error."""
+    spec = dict(wl.CONFIGS["tiny_decode"], qlen=4) if name == "tiny_decode_q4" else name
+    inp = wl.make_workload(spec, 0)
+    got = run_gpu(inp)
+    q = orc.decode_bf16(inp["q_bits"])
+    rows = 0
+    for i in range(inp["N"]):
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        S = int(inp["seq_lens"][i])
+        K = orc.gather_request_kv(inp["kv_bits"], "bf16", 1.0, inp["block_table"][i], S,
+                                  inp["W"], inp["block_size"])
+        for t in range(Q):
+            w = S - Q + 1 + t
+            go, gl = _window_oracle(q[qs + t], K, w, inp["sm_scale"])
+            dl = np.linalg.norm(got["lse"][qs + t] - gl)
+            do = np.linalg.norm(got["out"][qs + t] - go)
+            for wb in (w - 1, w + 1):
+                if wb < 1 or wb > S:
+                    continue
+                bo, bl = _window_oracle(q[qs + t], K, wb, inp["sm_scale"])
+                assert dl < np.linalg.norm(got["lse"][qs + t] - bl), (i, t, wb)
+                assert do < np.linalg.norm(got["out"][qs + t] - bo), (i, t, wb)
+            rows += 1
+    say(f"{name}: {rows} rows, each closest to its own window")
+    assert rows == inp["R"]
+
+
+def _wrong_row_lens(inp, row_lens, kind):
+    """The two wrong row views the pages reject, from the correct one:
+    subtract-offset (each row = the last row's local length minus its offset
+    from the last row) and committed-prefix-only (every row sees S - Q)."""
+    bad = row_lens.copy()
+    W = inp["W"]
+    for i in range(inp["N"]):
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        S = int(inp["seq_lens"][i])
+        for t in range(Q):
+            if kind == "subtract_offset":
+                bad[:, qs + t] = np.maximum(row_lens[:, qs + Q - 1] - (Q - 1 - t), 0)
+            else:
+                bad[:, qs + t] = np.bincount(np.arange(S - Q) % W, minlength=W)[:W]
+    return bad
+
+
+@pytest.mark.parametrize("kind", ["subtract_offset", "prefix_only"])
+def test_wrong_row_views_fail_the_bounds_on_the_gpu(kind):
+    """Negative controls on the verify workload: the kernels run with a wrong
+    row view (the correct table still covers every row) and their result
+    must then fail the stated bounds against the oracle somewhere -- the
+    parity checks above would catch either mistake."""
+    inp = named_workload("verify_dcp8")
+    dev = wl.to_device(inp)
+    plan = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
+                               dev["block_table"], dev["num_blocks"], dev["block_size"],
+                               dev["max_kv_seq_len"])
+    torch.cuda.synchronize()
+    bad = _wrong_row_lens(inp, plan["row_lens"].cpu().numpy(), kind)
+    bad_dev = torch.from_numpy(bad.astype(np.int32)).to("cuda")
+    parts = mla.mla_verify_attn(dev["q"], dev["kv"], bad_dev, plan["page_table"],
+                                dev["q_start"], page_size=plan["page_size"],
+                                max_qlen=dev["max_qlen"], nseg=1, sm_scale=dev["sm_scale"])
+    out, lse, _, _ = mla.mla_lse_merge(*parts, bad_dev, dev["q_start"],
+                                       page_size=plan["page_size"], H=inp["H"], nseg=1)
+    torch.cuda.synchronize()
+    out_ref, lse_ref = orc.verify_reference(inp)
+    d = np.abs(out.float().cpu().numpy() - out_ref)
+    dl = np.abs(lse.cpu().numpy() - lse_ref)
+    n_out = int((d > TOL_OUT["bf16"]).sum())
+    n_lse = int((dl > TOL_LSE).sum())
+    say(f"{kind}: {n_out}/{d.size} out elements over 1e-2 (max {d.max():.4f}), "
+        f"{n_lse}/{dl.size} lse over 1e-3 (max {dl.max():.4f})")
+    assert n_out > 0 and n_lse > 0
+
+
 @pytest.mark.parametrize("fmt", ["fp8_e4m3", "fp8_e5m2"])
 def test_fp8_every_finite_code_decodes(fmt):
     """Fill every used cache slot with codes cycling through all finite values
@@ -247,7 +335,7 @@ def test_fp8_every_finite_code_decodes(fmt):
     inp["kv_scale"] = 1.0 / float(np.max(np.abs(table[finite])))
     got = run_gpu(inp)
     out_ref, lse_ref = orc.verify_reference(inp)
-    assert out_excess(got["out"], out_ref, fmt) <= 1.0
+    check_out(got["out"], out_ref, fmt, "out")
     assert max_err(got["lse"], lse_ref) <= TOL_LSE
 
 
@@ -264,21 +352,16 @@ def test_side_stream_matches_default_stream():
 
 @pytest.mark.parametrize("name", wl.CONFIG_ORDER)
 def test_named_workload_parity(name):
-    """The five workloads at full size: plan bit-exact; out / lse against the
-    oracle on sampled requests (the longest and shortest included); every
-    output finite (cache slots outside any window hold NaN canaries)."""
+    """The five workloads at full size, every request: plan bit-exact; out /
+    lse against the oracle; every output finite (cache slots outside any
+    window hold NaN canaries)."""
     inp = named_workload(name)
     say(f"workload {name}: R={inp['R']} sum S={int(inp['seq_lens'].sum())}")
     got = run_gpu(inp)
     _check_plan(inp, got)
     assert np.all(np.isfinite(got["out"])) and np.all(np.isfinite(got["lse"]))
-    k = {"tiny_decode": 2, "verify_dcp8": 32, "fp8_verify_dcp4": 8,
-         "long_context_dcp8": 3, "ragged_mixed": 6}[name]
-    reqs = sample_requests(inp, k)
-    eo, el, ex, *_ = compare_requests(inp, got, reqs)
-    say(f"workload {name}: requests {reqs} max|dout|={eo:.3e} max|dlse|={el:.3e} "
-        f"excess={ex:.3f}")
-    assert ex <= 1.0
+    eo, el = compare_requests(inp, got, list(range(inp["N"])), f"{name} out")
+    say(f"workload {name}: all {inp['N']} requests max|dout|={eo:.3e} max|dlse|={el:.3e}")
     assert el <= TOL_LSE
 
 
@@ -306,11 +389,11 @@ def test_merge_paths(name):
     got = run_gpu(inp, want_shards=True)
     ref = _check_plan(inp, got)
     so, sl, _ = oracle_shard_results(inp, ref, spec["nseg"])
-    assert out_excess(got["shard_out"], so, "bf16") <= 1.0
+    check_out(got["shard_out"], so, "bf16", "shard_out")
     assert max_err(got["shard_lse"], sl) <= TOL_LSE
     out_ref, lse_ref = orc.verify_reference(inp)
-    say(f"  max|dout|={max_err(got['out'], out_ref):.3e} max|dlse|={max_err(got['lse'], lse_ref):.3e}")
-    assert out_excess(got["out"], out_ref, "bf16") <= 1.0
+    check_out(got["out"], out_ref, "bf16", "out")
+    say(f"  lse: max|d|={max_err(got['lse'], lse_ref):.3e}")
     assert max_err(got["lse"], lse_ref) <= TOL_LSE
 
 
@@ -318,11 +401,11 @@ def test_merge_paths(name):
 
 @pytest.mark.parametrize("W,I", [(1, 1), (3, 1), (4, 2)])
 def test_two_stage_verify_matches_one_stage_and_oracle(W, I):
-    """The SGLang decomposition (sharded committed prefix + one-shard dense
-    causal window of the verify tokens, merged by LSE) built from the same
-    native calls gives the per-row-window result: against the oracle's
-    definition, its own two-stage decomposition, and the one-stage path.
-    Request 0 has no committed token (S = Q)."""
+    """The SGLang decomposition (sharded committed prefix + one-source dense
+    causal window of the verify tokens, merged by LSE): the native two-stage
+    plan bit for bit against the oracle's, then the result against the
+    oracle's definition, its own two-stage decomposition, and the one-stage
+    path. Request 0 has no committed token (S = Q)."""
     spec = dict(N=4, H=16, qlens=[5, 1, 3, 4], seq_lens=[5, 40, 233, 77], block_size=16, W=W,
                 interleave=I, kv_dtype="bf16", nseg=1)
     inp = wl.make_workload(spec, seed=12, keep_logical=True)
@@ -331,12 +414,24 @@ def test_two_stage_verify_matches_one_stage_and_oracle(W, I):
     win = np.concatenate([inp["logical_kv_bits"][i][int(S) - int(Q):int(S)]
                           for i, (S, Q) in enumerate(zip(inp["seq_lens"], inp["qlens"]))])
     k_window = torch.from_numpy(win.view(np.int16)).view(torch.bfloat16).to("cuda")
-    out2, lse2 = mla.mla_verify_two_stage(dev, k_window)
+    qmax = dev["max_qlen"] + 2          # a window table wider than the longest window
+    plan = mla.mla_verify_two_stage_plan(dev["seq_lens"], dev["q_start"], dev["R"], W,
+                                         dev["block_table"], dev["num_blocks"],
+                                         dev["block_size"], dev["max_kv_seq_len"], qmax,
+                                         interleave=I)
+    dev2 = dict(dev, max_qlen=qmax)
+    out2, lse2, flag = mla.mla_verify_two_stage(dev2, k_window, plan=plan)
     torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    ref_plan = orc.two_stage_plan(inp["seq_lens"], inp["q_start"], W, inp["block_table"],
+                                  inp["block_size"], inp["max_kv_seq_len"], qmax, I)
+    assert np.array_equal(plan["row_lens"].cpu().numpy(), ref_plan["row_lens"])
+    assert np.array_equal(plan["page_table"].cpu().numpy(), ref_plan["page_table"])
+    assert np.array_equal(plan["window_table"].cpu().numpy(), ref_plan["window_table"])
     got_out = out2.float().cpu().numpy().astype(np.float64)
     got_lse = lse2.cpu().numpy().astype(np.float64)
     out_ref, lse_ref = orc.verify_reference(inp)
-    assert out_excess(got_out, out_ref, "bf16") <= 1.0
+    check_out(got_out, out_ref, "bf16", "two-stage out")
     assert max_err(got_lse, lse_ref) <= TOL_LSE
     q = orc.decode_bf16(inp["q_bits"])
     for i in range(inp["N"]):
@@ -344,11 +439,23 @@ def test_two_stage_verify_matches_one_stage_and_oracle(W, I):
         K = orc.decode_bf16(inp["logical_kv_bits"][i])
         o, l = orc.two_stage_verify(q[qs:qs + Q], K, int(inp["seq_lens"][i]), Q, W,
                                     inp["sm_scale"])
-        assert out_excess(got_out[qs:qs + Q], o, "bf16") <= 1.0
+        check_out(got_out[qs:qs + Q], o, "bf16", f"two-stage out, request {i}")
         assert max_err(got_lse[qs:qs + Q], l) <= TOL_LSE
     one = run_gpu(inp)
-    assert out_excess(got_out, one["out"], "bf16") <= 1.0
+    check_out(one["out"], out_ref, "bf16", "one-stage out")
     assert max_err(got_lse, one["lse"]) <= TOL_LSE
+    # the two-stage entry leaves the one-stage plan's checks in place: a
+    # request longer than the window table is flagged, not read out of bounds
+    bad = mla.mla_verify_two_stage_plan(dev["seq_lens"], dev["q_start"], dev["R"], W,
+                                        dev["block_table"], dev["num_blocks"],
+                                        dev["block_size"], dev["max_kv_seq_len"], 3,
+                                        interleave=I)
+    torch.cuda.synchronize()
+    assert int(bad["err_flag"].item()) & mla.MLA_PLAN_ERR_QLEN
+    L = bad["row_lens"].cpu().numpy()
+    qs0, Q0 = orc.request_rows(inp["q_start"], 0)       # Q = 5 > 3
+    assert np.all(L[:, qs0:qs0 + Q0] == 0)
+    assert np.all(bad["window_table"].cpu().numpy()[qs0:qs0 + Q0] == -1)
 
 
 # ------------------------------------------ one-segment (shard output) path ---
@@ -372,7 +479,9 @@ def _run_shards(inp, poison=True):
 def test_one_segment_path(name):
     """The one-segment path (segment merge folded into the attention kernel,
     then the shard merge alone) against the oracle's per-shard and final
-    results, and bit for bit against plan -> attn (nseg 1) -> lse_merge."""
+    results (each shard's output reaches the shard merge as bf16, so the
+    final bound includes that forced rounding); its per-shard results equal
+    those of plan -> attn (nseg 1) -> lse_merge bit for bit."""
     spec = dict(SMALL[name])
     inp = wl.make_workload(spec, seed=1)
     say(f"one-segment case {name} S={inp['seq_lens'].tolist()} Q={inp['qlens'].tolist()}")
@@ -382,34 +491,40 @@ def test_one_segment_path(name):
     g_so = got["shard_out"].float().numpy().astype(np.float64)
     g_sl = got["shard_lse"].numpy().astype(np.float64)
     assert not np.any(np.isnan(g_so)) and not np.any(np.isnan(g_sl))
-    assert out_excess(g_so, so, inp["kv_dtype"]) <= 1.0
+    check_out(g_so, so, inp["kv_dtype"], "shard_out")
     assert max_err(g_sl, sl) <= TOL_LSE
     out_ref, lse_ref = orc.verify_reference(inp)
     g_out = got["out"].float().numpy().astype(np.float64)
     assert np.all(np.isfinite(g_out)) and not np.any(np.isnan(got["lse"].numpy()))
-    assert out_excess(g_out, out_ref, inp["kv_dtype"]) <= 1.0
+    check_out(g_out, out_ref, inp["kv_dtype"], "out (bf16 hand-off)", shard_ref=so,
+              shard_lse_ref=sl, lse_ref=lse_ref)
     assert max_err(got["lse"].numpy(), lse_ref) <= TOL_LSE
-    # the split path with one segment computes the same per-shard and final bits
+    # the split path with one segment computes the same per-shard bits (its
+    # merge then keeps them in fp32, so only its final output may differ)
     split = run_gpu(inp, nseg=1, want_shards=True)
     assert np.array_equal(g_so, split["shard_out"])
     assert np.array_equal(g_sl, split["shard_lse"])
-    assert np.array_equal(g_out, split["out"])
-    assert np.array_equal(got["lse"].numpy().astype(np.float64), split["lse"])
+    assert max_err(got["lse"].numpy(), split["lse"]) <= 1e-5
 
 
 @pytest.mark.parametrize("name", ["tiny_decode", "verify_dcp8"])
 def test_one_segment_path_named_workload(name):
     """The one-segment path on the full-size workloads that run with one
-    segment: out / lse against the oracle on sampled requests."""
+    segment, every request: per-shard and final out / lse against the
+    oracle."""
     inp = named_workload(name)
     got = _run_shards(inp)
-    g = {"out": got["out"].float().numpy().astype(np.float64),
-         "lse": got["lse"].numpy().astype(np.float64)}
-    assert np.all(np.isfinite(g["out"])) and np.all(np.isfinite(g["lse"]))
-    reqs = sample_requests(inp, {"tiny_decode": 2, "verify_dcp8": 32}[name])
-    eo, el, ex, *_ = compare_requests(inp, g, reqs)
-    say(f"one-segment {name}: max|dout|={eo:.3e} max|dlse|={el:.3e} excess={ex:.3f}")
-    assert ex <= 1.0
+    g_out = got["out"].float().numpy().astype(np.float64)
+    g_lse = got["lse"].numpy().astype(np.float64)
+    assert np.all(np.isfinite(g_out)) and np.all(np.isfinite(g_lse))
+    so, sl, _ = oracle_shard_results(inp, oracle_plan(inp), 1, want_parts=False)
+    check_out(got["shard_out"].float().numpy(), so, "bf16", f"{name} shard_out")
+    assert max_err(got["shard_lse"].numpy(), sl) <= TOL_LSE
+    out_ref, lse_ref = orc.verify_reference(inp)
+    eo, _ = check_out(g_out, out_ref, "bf16", f"{name} out (bf16 hand-off)", shard_ref=so,
+                      shard_lse_ref=sl, lse_ref=lse_ref)
+    el = max_err(g_lse, lse_ref)
+    say(f"one-segment {name}: max|dout|={eo:.3e} max|dlse|={el:.3e}")
     assert el <= TOL_LSE
 
 
@@ -429,7 +544,7 @@ def test_shard_merge_alone_matches_oracle_merge(W):
     torch.cuda.synchronize()
     o_ref, l_ref = orc.lse_merge(so.double().numpy(), sl.double().numpy())
     got_o = out.float().cpu().numpy()
-    assert out_excess(got_o, o_ref, "bf16") <= 1.0
+    check_out(got_o, o_ref, "bf16", "shard merge out")
     assert max_err(lse.cpu().numpy(), l_ref) <= 1e-5
     assert np.all(got_o[2, 3] == 0.0) and lse[2, 3].item() == -float("inf")
 

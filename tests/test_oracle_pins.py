@@ -365,6 +365,50 @@ def test_two_stage_decomposition_equals_row_view():
         assert np.allclose(a[0], b[0], atol=1e-12) and np.allclose(a[1], b[1], atol=1e-12)
 
 
+@pytest.mark.parametrize("W,I", [(1, 1), (4, 1), (3, 2), (8, 1)])
+def test_two_stage_plan_splits_every_window(W, I):
+    """The two-stage plan's stage-1 lengths are the committed prefix on each
+    shard (they sum to S - Q, the same for every row of a request, and are a
+    prefix of each shard's local sequence: each equals the one-stage length of
+    a window of S - Q, computed by the closed form for I = 1), and stage 1 plus
+    stage 2 is exactly the one-stage window w = S - Q + 1 + t of every row.
+    The window table lists verify tokens q_start[i] .. q_start[i] + t."""
+    rng = np.random.default_rng(3 + W)
+    qlens = rng.integers(1, 8, size=6)
+    seq = qlens + rng.integers(0, 300, size=6)
+    seq[0] = qlens[0]                                   # empty committed prefix
+    q_start = np.concatenate([[0], np.cumsum(qlens)])
+    local = (seq // (I * W)) * I + np.minimum(seq % (I * W), I)
+    B = 16
+    nb = -(-local // B)
+    bt = np.full((6, int(nb.max())), -1)
+    perm = rng.permutation(int(nb.sum()) + 3)
+    off = 0
+    for i in range(6):
+        bt[i, :nb[i]] = perm[off:off + nb[i]]
+        off += int(nb[i])
+    qmax = int(qlens.max()) + 1
+    tp = orc.two_stage_plan(seq, q_start, W, bt, B, int(local.max()), qmax, I)
+    one = orc.row_view(seq, q_start, W, I)
+    L = tp["row_lens"]
+    for i in range(6):
+        qs, Q = orc.request_rows(q_start, i)
+        for t in range(Q):
+            rho = qs + t
+            assert L[:W, rho].sum() == seq[i] - Q
+            assert np.array_equal(L[:W, rho], L[:W, qs])
+            assert L[W, rho] == t + 1
+            assert L[:W, rho].sum() + L[W, rho] == one[:, rho].sum() == seq[i] - Q + 1 + t
+            assert np.all(L[:W, rho] <= one[:, rho])
+            if I == 1:
+                assert all(L[r, rho] == _closed_form_count(seq[i] - Q, r, W) for r in range(W))
+            assert list(tp["window_table"][rho]) == [qs + k if k <= t else -1
+                                                     for k in range(qmax)]
+    # stage-1 tables are the one-stage tables of the committed prefix
+    ref = orc.subpage_table(L[:W], bt, q_start, B, B, tp["pt_width"])
+    assert np.array_equal(tp["page_table"], ref)
+
+
 # -------------------------------------------------------------- segments ---
 
 @pytest.mark.parametrize("nseg,P", [(1, 16), (2, 16), (3, 4), (16, 4), (16, 1), (5, 128)])
@@ -476,6 +520,52 @@ def test_negative_controls_fail_tolerance(kind):
         bad, _ = orc.lse_merge(np.stack(outs), np.stack(lses))
         worst = max(worst, float(np.max(np.abs(bad - good))))
     assert worst > 1e-2
+
+
+def _bench_control(inp, kind):
+    """Max-abs out / lse errors and the count of out elements over 1e-2 of a
+    wrong row view over the whole workload, against the correct result."""
+    q = orc.decode_bf16(inp["q_bits"])
+    W = inp["W"]
+    wo, wl_, over = 0.0, 0.0, 0
+    for i in range(inp["N"]):
+        S = int(inp["seq_lens"][i])
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        K = orc.gather_request_kv(inp["kv_bits"], "bf16", 1.0, inp["block_table"][i], S, W,
+                                  inp["block_size"])
+        good, gl = orc.attention_rows(q[qs:qs + Q], K, S, Q, inp["sm_scale"])
+        L = _wrong_row_lens(S, Q, W, kind)
+        outs, lses = [], []
+        for r in range(W):
+            o, l = orc.shard_attention_rows(q[qs:qs + Q], orc.shard_local_kv(K, W, r), L[r],
+                                            inp["sm_scale"])
+            outs.append(o)
+            lses.append(l)
+        bad, bl = orc.lse_merge(np.stack(outs), np.stack(lses))
+        d = np.abs(bad - good)
+        wo = max(wo, float(d.max()))
+        wl_ = max(wl_, float(np.abs(bl - gl).max()))
+        over += int((d > 1e-2).sum())
+    return wo, wl_, over
+
+
+@pytest.mark.parametrize("name", ["tiny_decode_q4", "verify_dcp8"])
+def test_negative_controls_on_benchmark_shapes(name):
+    """P10 at the benchmark shapes: on the verify workload both wrong row views
+    exceed the stated bounds on out (1e-2) and lse (1e-3); on the tiny
+    decode shape with qlen 4 the committed-prefix-only view does, while
+    subtract-offset coincides with the correct view there (one shard: the last
+    row's length minus the offset is exactly each row's window)."""
+    spec = dict(wl.CONFIGS["tiny_decode"], qlen=4) if name == "tiny_decode_q4" else name
+    inp = wl.make_workload(spec, 0)
+    for kind in ("subtract_offset", "prefix_only"):
+        wo, wl_, over = _bench_control(inp, kind)
+        n = inp["R"] * inp["H"] * 512
+        print(f"{name} {kind}: max|dout|={wo:.4f} ({over}/{n} over 1e-2) max|dlse|={wl_:.4f}")
+        if name == "tiny_decode_q4" and kind == "subtract_offset":
+            assert wo == 0.0 and wl_ == 0.0
+        else:
+            assert wo > 1e-2 and wl_ > 1e-3 and over > 0
 
 
 def test_verify_reference_matches_row_view_pipeline():

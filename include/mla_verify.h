@@ -208,10 +208,11 @@ mla_status_t mla_verify_two_stage_plan(int32_t N, const int32_t* seq_lens,
  *              finite fp32 value, else MLA_ERR_INVALID
  *   row_lens, page_table, pt_width, page_size: from mla_verify_plan
  *   q_start    [N+1] as given to the plan
- *   max_qlen   the largest Q_i: it sizes the grid (ceil(max_qlen*H/64) row
- *              blocks per request). A smaller value is still correct (the
- *              extra row blocks of a longer request are taken in turn by the
- *              same workgroups), only slower.
+ *   max_qlen   >= every Q_i: it sizes the grid (ceil(max_qlen*H/64) row
+ *              blocks per request). The (row, head) pairs of a longer request
+ *              past that coverage get NaN partials (NaN shard outputs and
+ *              LSEs in mla_verify_attn_shard), which the merges carry into
+ *              out and lse: never an unwritten or silently wrong value.
  *   nseg       segments per (request, shard) group. Partition (a reading of
  *              the pages' tiles_per_segment = ceil(len/(nseg*TILE))): with Lg
  *              the group's longest row (its last), T = ceil(Lg/(nseg*P)) and

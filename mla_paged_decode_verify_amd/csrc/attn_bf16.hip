@@ -36,6 +36,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
   __shared__ RowExchange rx;
   WorkUnit u = decode_head(a, blockIdx.x);
   if (!u.valid) return;
+  poison_uncovered(a, u, threadIdx.x >> 6, threadIdx.x & 63);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -60,78 +61,71 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  // Row blocks m0, m0 + mblocks * 64, ... of the request (one unless its Q_i
-  // exceeds the caller's max_qlen, see decode_head).
-  for (bool first = true;; first = false) {
-    // ---- Q (through the second tile buffer: free until the first step's
-    // barrier, after which the next tile's loads target it), then the first tile
-    issue_q_tile(a, u, buf1, wave, lane, zero);
-    Bf16Pages pg;
-    if constexpr (SLICE) {
-      if (u.s != 0 || !first) vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
-      const SliceSrc v0 = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, 0), lo + 16 * wave, hi);
+  // ---- Q (through the second tile buffer: free until the first step's
+  // barrier, after which the next tile's loads target it), then the first tile
+  issue_q_tile(a, u, buf1, wave, lane, zero);
+  Bf16Pages pg;
+  if constexpr (SLICE) {
+    if (u.s != 0) vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
+    const SliceSrc v0 = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, 0), lo + 16 * wave, hi);
 #pragma unroll
-      for (int j = 0; j < 18; ++j) issue_slice(v0, zero, buf0, wave, lane, j);
-    } else {
-      pg.fetch(a, pt_row, lo, hi, wave, lane);
-      issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane, zero);
-    }
-    int mrow, hi_row;
-    bool row_ok;
-    lane_row(a, u, g, lane, mrow, hi_row, row_ok);
-    const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
-    WaveState st;
-    state_init(st);
-    MLA_WAIT_VMCNT(0);
-    lds_barrier();
-    bf16x8 qf[kQSteps];
-    read_q(buf1, g, lane, qf);
-
-    // One tile (index kt from the segment start): wait until `cur` holds it,
-    // start filling `nxt` with the next tile, compute on `cur`.
-    auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
-      const bool more = tb + kTile < hi;
-      MLA_WAIT_VMCNT(0);                      // this wave's loads of `cur` have landed ...
-      lds_barrier();                          // ... for every wave; `nxt` is no longer read
-      SliceSrc v{zero, 0};
-      if constexpr (SLICE) {
-        if (more) {
-          const int nk = kt + 1;
-          if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
-          v = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile + 16 * wave, hi);
-        }
-      } else {
-        if (more) {
-          pg.fetch(a, pt_row, tb + kTile, hi, wave, lane);
-          issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane, zero);
-        }
-      }
-      // one load every other QK K-step: the next tile's data goes out early,
-      // and its LDS writes are spread over the whole QK product, which competes
-      // with them for LDS bandwidth (measured: faster than packing the loads
-      // into the first half, or issuing them in the PV product)
-      auto issue = [&](int j) {
-        if constexpr (SLICE) {
-          if (more && (j & 1) == 0) issue_slice(v, zero, nxt, wave, lane, j >> 1);
-        }
-      };
-      if (idle)
-        idle_tile(issue);
-      else
-        compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
-    };
-    int kt = 0;
-    for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
-      step(buf0, buf1, tb, kt);
-      if (tb + kTile >= hi) break;
-      step(buf1, buf0, tb + kTile, kt + 1);
-    }
-
-    store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);
-    u.m0 += a.mblocks * kAttnRows;
-    if (u.m0 >= u.M) break;
-    __syncthreads();                          // the staged outputs have been read
+    for (int j = 0; j < 18; ++j) issue_slice(v0, zero, buf0, wave, lane, j);
+  } else {
+    pg.fetch(a, pt_row, lo, hi, wave, lane);
+    issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, lane, zero);
   }
+  int mrow, hi_row;
+  bool row_ok;
+  lane_row(a, u, g, lane, mrow, hi_row, row_ok);
+  const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
+  WaveState st;
+  state_init(st);
+  MLA_WAIT_VMCNT(0);
+  lds_barrier();
+  bf16x8 qf[kQSteps];
+  read_q(buf1, g, lane, qf);
+
+  // One tile (index kt from the segment start): wait until `cur` holds it,
+  // start filling `nxt` with the next tile, compute on `cur`.
+  auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
+    const bool more = tb + kTile < hi;
+    MLA_WAIT_VMCNT(0);                      // this wave's loads of `cur` have landed ...
+    lds_barrier();                          // ... for every wave; `nxt` is no longer read
+    SliceSrc v{zero, 0};
+    if constexpr (SLICE) {
+      if (more) {
+        const int nk = kt + 1;
+        if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
+        v = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile + 16 * wave, hi);
+      }
+    } else {
+      if (more) {
+        pg.fetch(a, pt_row, tb + kTile, hi, wave, lane);
+        issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, lane, zero);
+      }
+    }
+    // one load every other QK K-step: the next tile's data goes out early,
+    // and its LDS writes are spread over the whole QK product, which competes
+    // with them for LDS bandwidth (measured: faster than packing the loads
+    // into the first half, or issuing them in the PV product)
+    auto issue = [&](int j) {
+      if constexpr (SLICE) {
+        if (more && (j & 1) == 0) issue_slice(v, zero, nxt, wave, lane, j >> 1);
+      }
+    };
+    if (idle)
+      idle_tile(issue);
+    else
+      compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
+  };
+  int kt = 0;
+  for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
+    step(buf0, buf1, tb, kt);
+    if (tb + kTile >= hi) break;
+    step(buf1, buf0, tb + kTile, kt + 1);
+  }
+
+  store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);
 }
 
 }  // namespace

@@ -204,9 +204,7 @@ struct WorkUnit {
 // block) get consecutive ids on that XCD, so they run side by side: its Q,
 // and each unit's KV across row blocks, come from HBM into that XCD's L2
 // once. The grid covers ceil(N / 8) * 8 requests and mblocks row blocks per
-// request; a request with more (row, head) pairs than that (its Q_i above the
-// caller's max_qlen) has them covered too: unit mb also takes row blocks
-// mb + mblocks, mb + 2 mblocks, ... so no output is left unwritten.
+// request (see poison_uncovered for a request with more).
 __device__ inline WorkUnit decode_head(const AttnArgs& a, int b) {
   WorkUnit u;
   const int slot = b >> 3;
@@ -313,6 +311,11 @@ __device__ __forceinline__ void issue_q_tile(const AttnArgs& a, const WorkUnit& 
 //    already the B operand of the wave's own K-step s, so P never moves
 //    between lanes; the V^T operand takes the same token order from two
 //    transposed 4-token reads (ds_read_b64_tr_b16) per instruction.
+//  * The weights enter the PV product as bf16 (the operand format of the
+//    matrix cores next to a bf16 V): each is rounded by at most 2^-8 of its
+//    value, so the output moves by at most 2^-8 of the softmax-weighted mean
+//    of |v|. (Feeding them as two bf16 terms, hi + lo, removes that but
+//    doubles the PV instructions: measured 22-33 % slower.)
 //
 // Online softmax in base 2 with a lazily refreshed reference: O and the sum
 // are rescaled only when the row maximum passes the reference by more than 8
@@ -529,22 +532,49 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// A unit with no token to read, for all its row blocks (see decode_head):
-// in the one-segment form its rows still get their (empty) shard results,
-// o_r = 0 and lse_r = -inf; in the split form a segment the merge reads gets
-// the empty partials (maximum -inf, sum 0: the merge then gives it weight 0
-// and never touches its output), and any other segment nothing.
+// A unit with no token to read: in the one-segment form its rows still get
+// their (empty) shard results, o_r = 0 and lse_r = -inf; in the split form a
+// segment the merge reads gets the empty partials (maximum -inf, sum 0: the
+// merge then gives it weight 0 and never touches its output), and any other
+// segment nothing.
 __device__ inline void store_empty(const AttnArgs& a, const WorkUnit& u, int wave, int lane) {
   const int64_t base = ((int64_t)u.r * a.R + u.qs) * a.H;
-  for (int m0 = u.m0; m0 < u.M; m0 += a.mblocks * kAttnRows) {
-    for (int k = wave; k < kAttnRows && m0 + k < u.M; k += 4) {
-      const int64_t e = base + m0 + k;
-      if (a.shard_out != nullptr) {
-        *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
-        if (lane == 0) a.shard_lse[e] = kNegInf;
-      } else if (u.read && lane == 0) {
-        a.segm_max[e * a.nseg + u.s] = kNegInf;
-        a.segm_expsum[e * a.nseg + u.s] = 0.f;
+  for (int k = wave; k < kAttnRows && u.m0 + k < u.M; k += 4) {
+    const int64_t e = base + u.m0 + k;
+    if (a.shard_out != nullptr) {
+      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
+      if (lane == 0) a.shard_lse[e] = kNegInf;
+    } else if (u.read && lane == 0) {
+      a.segm_max[e * a.nseg + u.s] = kNegInf;
+      a.segm_expsum[e * a.nseg + u.s] = 0.f;
+    }
+  }
+}
+
+// A request with more (row, head) pairs than the grid's mblocks row blocks
+// cover (its Q_i above the caller's max_qlen) must not end in unwritten
+// outputs: the unit of its last covered row block fills every uncovered
+// pair's results for its shard and segment with NaN (written as bits, so no
+// fast-math folding applies), which both merges carry into out and lse.
+__device__ inline void poison_uncovered(const AttnArgs& a, const WorkUnit& u, int wave, int lane) {
+  const int covered = a.mblocks * kAttnRows;
+  if (u.mb != a.mblocks - 1 || u.M <= covered) return;   // uniform
+  const uint32_t qnan = 0x7FC00000u;
+  const int64_t base = ((int64_t)u.r * a.R + u.qs) * a.H;
+  for (int m = covered + wave; m < u.M; m += 4) {
+    const int64_t e = base + m;
+    if (a.shard_out != nullptr) {
+      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) =
+          make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+      if (lane == 0) reinterpret_cast<uint32_t*>(a.shard_lse)[e] = qnan;
+    } else {
+      const int64_t f = e * a.nseg + u.s;
+      uint32_t* o = reinterpret_cast<uint32_t*>(a.segm_out + f * kVDim) + 8 * lane;
+      *reinterpret_cast<uint4*>(o) = make_uint4(qnan, qnan, qnan, qnan);
+      *reinterpret_cast<uint4*>(o + 4) = make_uint4(qnan, qnan, qnan, qnan);
+      if (lane == 0) {
+        reinterpret_cast<uint32_t*>(a.segm_max)[f] = qnan;
+        reinterpret_cast<uint32_t*>(a.segm_expsum)[f] = qnan;
       }
     }
   }

@@ -130,6 +130,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   __shared__ RowExchange rx;
   WorkUnit u = decode_head(a, blockIdx.x);
   if (!u.valid) return;
+  poison_uncovered(a, u, threadIdx.x >> 6, threadIdx.x & 63);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,74 +156,66 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   }
   const int ntiles = (hi - lo + kTile - 1) / kTile;
 
-  // Row blocks m0, m0 + mblocks * 64, ... of the request (one unless its Q_i
-  // exceeds the caller's max_qlen, see decode_head).
-  for (bool first = true;; first = false) {
-    // ---- Q, staged in the tile buffer
-    issue_q_tile(a, u, buf, wave, lane, zero);
+  // ---- Q, staged in the tile buffer
+  issue_q_tile(a, u, buf, wave, lane, zero);
 
-    auto issue_tile = [&](int t) {
-      unsigned char* st = stage + (t & 1) * kF8Tile;
-      const int tb = lo + t * kTile;
-      if constexpr (SLICE) {
-        if ((t & 63) == 0 && (t != 0 || u.s != 0 || !first))
-          vpg = f8_slice_pages(a, pt_row, tb, hi, wave, lane);
-        const int32_t sp = __builtin_amdgcn_readlane(vpg, t & 63);
-        F8Slice v;
-        const bool ok = sp >= 0 && sp < a.num_subpages;
-        const int t0 = tb + 16 * wave;
-        v.nvalid = ok ? min(max(hi - t0, 0), 16) : 0;
-        v.base = pool + (((int64_t)(ok ? sp : 0) << a.page_shift) + (t0 & (a.page_size - 1))) *
-                            kHeadDim;
+  auto issue_tile = [&](int t) {
+    unsigned char* st = stage + (t & 1) * kF8Tile;
+    const int tb = lo + t * kTile;
+    if constexpr (SLICE) {
+      if ((t & 63) == 0 && (t != 0 || u.s != 0)) vpg = f8_slice_pages(a, pt_row, tb, hi, wave, lane);
+      const int32_t sp = __builtin_amdgcn_readlane(vpg, t & 63);
+      F8Slice v;
+      const bool ok = sp >= 0 && sp < a.num_subpages;
+      const int t0 = tb + 16 * wave;
+      v.nvalid = ok ? min(max(hi - t0, 0), 16) : 0;
+      v.base = pool + (((int64_t)(ok ? sp : 0) << a.page_shift) + (t0 & (a.page_size - 1))) *
+                          kHeadDim;
 #pragma unroll
-        for (int j = 0; j < kF8Loads; ++j) issue_f8_slice(v, zero, st, wave, lane, j);
-      } else {
+      for (int j = 0; j < kF8Loads; ++j) issue_f8_slice(v, zero, st, wave, lane, j);
+    } else {
 #pragma unroll
-        for (int j = 0; j < kF8Loads; ++j)
-          issue_f8_pages(a, pool, pt_row, tb, hi, zero, st, wave, lane, j);
-      }
-    };
-
-    // ---- tiles 0 and 1 in flight with Q; Q into registers; tile 0 widened
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    int mrow, hi_row;
-    bool row_ok;
-    lane_row(a, u, g, lane, mrow, hi_row, row_ok);
-    const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
-    WaveState st;
-    state_init(st);
-    MLA_WAIT_VMCNT(0);
-    lds_barrier();
-    bf16x8 qf[kQSteps];
-    read_q(buf, g, lane, qf);
-    lds_barrier();                            // every wave holds its Q: the buffer is free
-    widen_tile<E5M2>(stage, buf, tid);
-    lds_barrier();                            // tile 0 in the buffer; staging tile 0 is free
-    if (ntiles > 2) issue_tile(2);
-
-    for (int k = 0; k < ntiles; ++k) {
-      if (idle)
-        idle_tile([](int) {});
-      else
-        compute_tile(buf, &px, qf, st, lo + k * kTile, hi_row, a.qk_scale_log2, g, c, lane,
-                     [](int) {});
-      if (k + 1 < ntiles) {
-        // tile k + 1 has landed (this wave's later loads: tile k + 2's nine)
-        if (k + 2 < ntiles) MLA_WAIT_VMCNT(kF8Loads); else MLA_WAIT_VMCNT(0);
-        lds_barrier();                        // ... for every wave; the buffer is no longer read
-        widen_tile<E5M2>(stage + ((k + 1) & 1) * kF8Tile, buf, tid);
-        lds_barrier();                        // tile k + 1 in the buffer; its staging tile is free
-        if (k + 3 < ntiles) issue_tile(k + 3);
-      }
+      for (int j = 0; j < kF8Loads; ++j)
+        issue_f8_pages(a, pool, pt_row, tb, hi, zero, st, wave, lane, j);
     }
+  };
 
-    // row group 0 stages its O in the tile buffer, row group 1 in the staging tiles
-    store_partials(a, u, st, rx, g == 0 ? buf : stage, mrow, row_ok, g, c, lane);
-    u.m0 += a.mblocks * kAttnRows;
-    if (u.m0 >= u.M) break;
-    __syncthreads();                          // the staged outputs have been read
+  // ---- tiles 0 and 1 in flight with Q; Q into registers; tile 0 widened
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  int mrow, hi_row;
+  bool row_ok;
+  lane_row(a, u, g, lane, mrow, hi_row, row_ok);
+  const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
+  WaveState st;
+  state_init(st);
+  MLA_WAIT_VMCNT(0);
+  lds_barrier();
+  bf16x8 qf[kQSteps];
+  read_q(buf, g, lane, qf);
+  lds_barrier();                            // every wave holds its Q: the buffer is free
+  widen_tile<E5M2>(stage, buf, tid);
+  lds_barrier();                            // tile 0 in the buffer; staging tile 0 is free
+  if (ntiles > 2) issue_tile(2);
+
+  for (int k = 0; k < ntiles; ++k) {
+    if (idle)
+      idle_tile([](int) {});
+    else
+      compute_tile(buf, &px, qf, st, lo + k * kTile, hi_row, a.qk_scale_log2, g, c, lane,
+                   [](int) {});
+    if (k + 1 < ntiles) {
+      // tile k + 1 has landed (this wave's later loads: tile k + 2's nine)
+      if (k + 2 < ntiles) MLA_WAIT_VMCNT(kF8Loads); else MLA_WAIT_VMCNT(0);
+      lds_barrier();                        // ... for every wave; the buffer is no longer read
+      widen_tile<E5M2>(stage + ((k + 1) & 1) * kF8Tile, buf, tid);
+      lds_barrier();                        // tile k + 1 in the buffer; its staging tile is free
+      if (k + 3 < ntiles) issue_tile(k + 3);
+    }
   }
+
+  // row group 0 stages its O in the tile buffer, row group 1 in the staging tiles
+  store_partials(a, u, st, rx, g == 0 ? buf : stage, mrow, row_ok, g, c, lane);
 }
 
 static_assert(2 * kF8Tile >= 32 * kStageRow, "a row group's O fits the two staging tiles");

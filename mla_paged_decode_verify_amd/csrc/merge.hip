@@ -62,9 +62,15 @@ __device__ inline uint32_t pack2_bf16(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// Maximum that keeps a NaN (fmaxf drops it): partials of rows the attention
+// grid did not cover are NaN, and must reach out and lse as NaN.
+__device__ inline float max_keep_nan(float m, float x) {
+  return (m != m || x != x) ? __builtin_nanf("") : fmaxf(m, x);
+}
+
 __device__ inline float wave_max(float x) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  for (int o = 32; o > 0; o >>= 1) x = max_keep_nan(x, __shfl_xor(x, o));
   return x;
 }
 __device__ inline float wave_sum(float x) {
@@ -174,16 +180,16 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
       float* m = sm + r * nseg;
       float* c = sc + r * nseg;
       float M = kNegInf;
-      for (int s = 0; s < nact; ++s) M = fmaxf(M, m[s]);
+      for (int s = 0; s < nact; ++s) M = max_keep_nan(M, m[s]);
       float E = 0.f;
       if (M != kNegInf)
         for (int s = 0; s < nact; ++s) E += c[s] * __builtin_amdgcn_exp2f(m[s] - M);
-      const bool live = M != kNegInf && E > 0.f;
+      const bool live = M != kNegInf && !(E <= 0.f);   // NaN stays NaN
       const float inv = live ? 1.f / E : 0.f;
       for (int s = 0; s < nseg; ++s)
         c[s] = live && s < nact ? __builtin_amdgcn_exp2f(m[s] - M) * inv : 0.f;
       const float l = live ? kLn2 * (M + __log2f(E)) : kNegInf;
-      gm = fmaxf(gm, l);
+      gm = max_keep_nan(gm, l);
       sl[r] = l;
     }
     // ---- shard weights: exp(lse_r - G) / sum, G the largest LSE
@@ -250,7 +256,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
                                      a.row_lens[(int64_t)r * a.R + rho], nseg, a.page_size);
     const int64_t base = r * rstride + pbase;
     float M = kNegInf;
-    for (int s = 0; s < nact; ++s) M = fmaxf(M, a.segm_max[base + s]);
+    for (int s = 0; s < nact; ++s) M = max_keep_nan(M, a.segm_max[base + s]);
     float o[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) o[k] = 0.f;
@@ -262,7 +268,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
         E += a.segm_expsum[base + s] * c;
         axpy8(o, c, a.segm_out + (base + s) * kVDim + 8 * lane);
       }
-      if (E > 0.f) {
+      if (!(E <= 0.f)) {                   // NaN stays NaN
         const float inv = 1.f / E;
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] *= inv;
@@ -274,6 +280,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
     }
     store_shard(a, r, rho, h, lane, o, lse_r);
     if (lse_r == kNegInf) continue;          // empty shard contributes nothing
+    if (lse_r != lse_r) gmax = lse_r;         // NaN (an uncovered row) stays NaN
     if (lse_r > gmax) {
       const float f = __expf(gmax - lse_r);  // gmax = -inf gives 0
 #pragma unroll
@@ -327,7 +334,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) shard_merge_kernel(ShardMerg
       if (j < W) v[j] = *reinterpret_cast<const uint4*>(src + j * rs * kVDim);
     float G = kNegInf;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) G = fmaxf(G, l[j]);
+    for (int j = 0; j < 8; ++j) G = max_keep_nan(G, l[j]);
     float lse_out = kNegInf;
     float w[8];
 #pragma unroll
@@ -361,7 +368,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) shard_merge_kernel(ShardMerg
   for (int r = lane; r < W; r += 64) {
     const float l = a.shard_lse[r * rs + pair];
     sw[r] = l;
-    gm = fmaxf(gm, l);
+    gm = max_keep_nan(gm, l);
   }
   const float G = wave_max(gm);
   float lse_out = kNegInf;

@@ -285,7 +285,7 @@ def gather_request_kv(cache, kv_dtype: str, kv_scale: float, block_table_row,
 # Attention: the definition, per-shard pieces, segments, merges
 # --------------------------------------------------------------------------
 
-def attention_rows(q_rows, K, seq_len: int, qlen: int, sm_scale: float):
+def attention_rows(q_rows, K, seq_len: int, qlen: int, sm_scale: float, values=None):
     """Causal multi-token verify attention for one request (the definition).
 
     q_rows [Q, H, 576], K [S, 576] (logical, dequantised). Row t attends to
@@ -295,11 +295,14 @@ def attention_rows(q_rows, K, seq_len: int, qlen: int, sm_scale: float):
     [Q, H, 512] and the natural-log LSE [Q, H] of the scaled scores
     ([S34432] implementation item 1 and review item 4: LSE base e).
     Q = 1 is plain decode ([V51705] implementation item 4).
+    ``values`` [S, n] replaces V (default K[:, :512]): the same softmax
+    weights applied to other per-position values, e.g. |V| for an error bound.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
+    V = K[:, :V_DIM] if values is None else np.asarray(values, dtype=np.float64)
     Q, H, _ = q_rows.shape
-    out = np.zeros((Q, H, V_DIM))
+    out = np.zeros((Q, H, V.shape[1]))
     lse = np.zeros((Q, H))
     for t in range(Q):
         w = window_length(seq_len, qlen, t)
@@ -307,7 +310,7 @@ def attention_rows(q_rows, K, seq_len: int, qlen: int, sm_scale: float):
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
         z = p.sum(axis=1)
-        out[t] = (p @ K[:w, :V_DIM]) / z[:, None]
+        out[t] = (p @ V[:w]) / z[:, None]
         lse[t] = m[:, 0] + np.log(z)
     return out, lse
 
@@ -320,17 +323,19 @@ def shard_local_kv(K, W: int, r: int, interleave: int = 1):
     return K[shard_of(p, W, interleave) == r]
 
 
-def shard_attention_rows(q_rows, K_local, L_rows, sm_scale: float):
+def shard_attention_rows(q_rows, K_local, L_rows, sm_scale: float, values=None):
     """Rank-local attention of each row over the first L local tokens.
 
     Each row's window restricted to one shard is a prefix of that shard's
     local sequence ([V51705] Implementation breakdown item 2: the local length
     is the count of window positions the shard holds). An empty prefix gives
-    out 0 and lse -inf (a reading: nothing to attend to).
+    out 0 and lse -inf (a reading: nothing to attend to). ``values`` replaces
+    V as in attention_rows.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
+    V = K_local[:, :V_DIM] if values is None else np.asarray(values, dtype=np.float64)
     Q, H, _ = q_rows.shape
-    out = np.zeros((Q, H, V_DIM))
+    out = np.zeros((Q, H, V.shape[1]))
     lse = np.full((Q, H), -np.inf)
     for t in range(Q):
         L = int(L_rows[t])
@@ -340,13 +345,13 @@ def shard_attention_rows(q_rows, K_local, L_rows, sm_scale: float):
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
         z = p.sum(axis=1)
-        out[t] = (p @ K_local[:L, :V_DIM]) / z[:, None]
+        out[t] = (p @ V[:L]) / z[:, None]
         lse[t] = m[:, 0] + np.log(z)
     return out, lse
 
 
 def segment_partials(q_rows, K_local, L_rows, nseg: int, page_size: int,
-                     sm_scale: float):
+                     sm_scale: float, values=None):
     """Split-K partials of one (request, shard) group.
 
     [V51705] Implementation breakdown item 4 and the merge snippet: the
@@ -361,14 +366,16 @@ def segment_partials(q_rows, K_local, L_rows, nseg: int, page_size: int,
 
     Returns m2 [Q, H, nseg] (max of scaled score * log2 e), e [Q, H, nseg]
     (sum of 2^(score2 - m2)), O [Q, H, nseg, 512], active [Q, nseg].
+    ``values`` replaces V as in attention_rows (O then has its width).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
+    V = K_local[:, :V_DIM] if values is None else np.asarray(values, dtype=np.float64)
     Q, H, _ = q_rows.shape
     Lg = int(max(L_rows)) if Q else 0
     span = -(-Lg // (nseg * page_size)) * page_size   # T * P tokens
     m2 = np.full((Q, H, nseg), -np.inf)
     e = np.zeros((Q, H, nseg))
-    O = np.zeros((Q, H, nseg, V_DIM))
+    O = np.zeros((Q, H, nseg, V.shape[1]))
     active = np.zeros((Q, nseg), dtype=bool)
     for t in range(Q):
         L = int(L_rows[t])
@@ -383,7 +390,7 @@ def segment_partials(q_rows, K_local, L_rows, nseg: int, page_size: int,
             w = np.exp2(s2 - mx[:, None])
             m2[t, :, s] = mx
             e[t, :, s] = w.sum(axis=1)
-            O[t, :, s] = w @ K_local[lo:hi, :V_DIM]
+            O[t, :, s] = w @ V[lo:hi]
     return m2, e, O, active
 
 

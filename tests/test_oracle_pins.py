@@ -294,6 +294,53 @@ def test_attention_matches_torch_sdpa(S, Q, scale):
     assert np.allclose(out, lib_out, atol=1e-10, rtol=0)
 
 
+def test_attention_values_argument():
+    """values = K[:, :512] is the default; values = |V| matches torch's SDPA
+    with |V| as the value tensor (the weights are the same softmax)."""
+    S, Q, H, scale = 40, 3, 4, 0.1
+    q = _rand((Q, H, 576), 7)
+    K = _rand((S, 576), 8)
+    a = orc.attention_rows(q, K, S, Q, scale)
+    b = orc.attention_rows(q, K, S, Q, scale, values=K[:, :512])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c, _ = orc.attention_rows(q, K, S, Q, scale, values=np.abs(K[:, :512]))
+    mask = torch.zeros(Q, S, dtype=torch.bool)
+    for t in range(Q):
+        mask[t, :S - Q + 1 + t] = True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), torch.from_numpy(K)[None].expand(H, -1, -1),
+        torch.from_numpy(np.abs(K[:, :512]))[None].expand(H, -1, -1), attn_mask=mask,
+        scale=scale).permute(1, 0, 2).numpy()
+    assert np.allclose(c, ref, atol=1e-12, rtol=0)
+    assert np.all(c >= np.abs(a[0]) - 1e-12)          # triangle inequality
+    L = [S // 2, S // 3, 0]
+    d, l = orc.shard_attention_rows(q, K, L, scale, values=np.abs(K[:, :512]))
+    assert np.all(d[2] == 0) and np.all(np.isneginf(l[2]))
+    e, _ = orc.attention_rows(q[:1], K, L[0], 1, scale, values=np.abs(K[:, :512]))
+    assert np.allclose(d[0], e[0], atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 3, 7, 64, 4000])
+def test_bf16_weight_rounding_bound(n):
+    """The bound the GPU parity tests use for the bf16 softmax weights fed to
+    the matrix cores: rounding every weight p_j to bf16 (nearest even) moves
+    sum_j p_j v_j / sum_j p_j by at most 2^-8 sum_j w_j |v_j|, w = p / sum p
+    (each |bf16(p) - p| <= 2^-8 p). Checked on random logits and values, with
+    the weights rounded by torch's own bf16 conversion."""
+    rng = np.random.default_rng(n)
+    worst = 0.0
+    for trial in range(50):
+        x = rng.normal(0.0, 1.5, n)
+        p = np.exp2(x - x.max() + rng.uniform(0, 8))       # the lazy reference: p up to 2^8
+        v = rng.normal(0.0, 1.0, (n, 64)) * rng.choice([1.0, 4.0], (n, 1))
+        ph = torch.from_numpy(p).to(torch.bfloat16).double().numpy()
+        err = np.abs((ph - p) @ v) / p.sum()
+        bound = 2.0 ** -8 * ((p / p.sum()) @ np.abs(v))
+        assert np.all(err <= bound * (1 + 1e-12))
+        worst = max(worst, float(np.max(err / bound)))
+    assert worst > 0.05        # the bound is not vacuous for short windows
+
+
 @pytest.mark.parametrize("W,I", [(1, 1), (2, 1), (3, 1), (4, 1), (8, 1), (2, 2), (3, 4), (4, 3)])
 def test_sharded_then_merged_equals_unsharded(W, I):
     """P5: per-shard rank-local attention over the row view, merged by

@@ -22,7 +22,8 @@
  * Conventions for every call below.
  *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays,
  *     allocated and owned by the caller. The library allocates no device
- *     memory and keeps no state except a thread-local error string.
+ *     memory at run time and keeps no state except a thread-local error
+ *     string and the static scratch array of mla_verify_attn_merge_static.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; 0 = the
  *     default stream). Nothing synchronises.
  *   - Scalar arguments are validated on the host before anything is
@@ -293,6 +294,59 @@ mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
                            int32_t R, int32_t H, int32_t W, int32_t nseg,
                            void* shard_out, float* shard_lse, void* out,
                            float* lse, void* stream);
+
+/*
+ * Attention, segment merge and shard merge in one call ([V51705]
+ * Implementation breakdown item 4 and the merge snippet; [S34432] review
+ * item 4): mla_verify_attn into a caller workspace, then mla_lse_merge from
+ * it, on `stream`. The same results, bit for bit, as those two calls.
+ *
+ *   q ... nseg   as for mla_verify_attn (same checks, same error codes)
+ *   workspace    device memory of at least mla_verify_workspace_bytes(W, R,
+ *                H, nseg) bytes, 16-byte aligned, laid out segm_out |
+ *                segm_max | segm_expsum; its contents on entry do not
+ *                matter, and on return it holds the partials
+ *   out          [R, H, 512] bf16, 16-byte aligned;  lse [R, H] fp32
+ */
+mla_status_t mla_verify_attn_merge(const void* q, const void* kv,
+                                   int64_t num_blocks, int32_t block_size,
+                                   int32_t page_size, mla_kv_dtype_t kv_dtype,
+                                   float kv_scale, float sm_scale,
+                                   const int32_t* row_lens,
+                                   const int32_t* page_table, int32_t pt_width,
+                                   const int32_t* q_start, int32_t N, int32_t R,
+                                   int32_t H, int32_t W, int32_t max_qlen,
+                                   int32_t nseg, void* workspace,
+                                   size_t workspace_bytes, void* out,
+                                   float* lse, void* stream);
+
+/* Size of the library's static scratch array (per GPU). */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mla_verify_attn_merge without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the partials go to a static scratch array
+ * of MLA_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU it
+ * runs on until the process ends. The call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine). Sizes whose partials exceed
+ * the array (mla_verify_workspace_bytes(W, R, H, nseg) > 64 MiB) return
+ * MLA_ERR_INVALID before anything is launched. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (on different streams, or
+ * from different threads) race and must be ordered by the caller. Nothing in
+ * the array needs to start at zero. Same arguments, checks and results as
+ * mla_verify_attn_merge otherwise.
+ */
+mla_status_t mla_verify_attn_merge_static(const void* q, const void* kv,
+                                          int64_t num_blocks, int32_t block_size,
+                                          int32_t page_size,
+                                          mla_kv_dtype_t kv_dtype, float kv_scale,
+                                          float sm_scale, const int32_t* row_lens,
+                                          const int32_t* page_table,
+                                          int32_t pt_width, const int32_t* q_start,
+                                          int32_t N, int32_t R, int32_t H, int32_t W,
+                                          int32_t max_qlen, int32_t nseg, void* out,
+                                          float* lse, void* stream);
 
 /*
  * Shard merge alone ([V51705] Motivation: rank-local results combine through

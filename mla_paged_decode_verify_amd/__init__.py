@@ -199,6 +199,66 @@ def mla_verify_attn_shard(q, kv, row_lens, page_table, q_start, *, page_size, ma
     return shard_out, shard_lse
 
 
+def _attn_merge_args(q, kv, row_lens, page_table, q_start, out, lse):
+    _dev(q, torch.bfloat16, "q")
+    _dev(kv, None, "kv")
+    _dev(row_lens, torch.int32, "row_lens")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(q_start, torch.int32, "q_start")
+    R, H, D = q.shape
+    W, num_blocks, block_size, D2 = kv.shape
+    if D != HEAD_DIM or D2 != HEAD_DIM:
+        raise ValueError("head dim must be 576")
+    if tuple(row_lens.shape) != (W, R) or page_table.shape[:2] != (W, R):
+        raise ValueError("plan tensors do not match q / kv")
+    if out is None:
+        out = torch.empty((R, H, V_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((R, H), dtype=torch.float32, device=q.device)
+    _dev(out, torch.bfloat16, "out")
+    _dev(lse, torch.float32, "lse")
+    if out.numel() != R * H * V_DIM or lse.numel() != R * H:
+        raise ValueError("out / lse have the wrong size")
+    return R, H, W, num_blocks, block_size, out, lse
+
+
+def mla_verify_attn_merge(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen, nseg,
+                          sm_scale, kv_scale=1.0, workspace=None, out=None, lse=None,
+                          stream=None):
+    """Attention + segment merge + shard merge in one call, the split-K
+    partials in ``workspace`` (a device tensor of at least
+    mla_verify_workspace_bytes(W, R, H, nseg) bytes; allocated here if not
+    given). Returns (out [R,H,512] bf16, lse [R,H] fp32)."""
+    R, H, W, num_blocks, block_size, out, lse = _attn_merge_args(q, kv, row_lens, page_table,
+                                                                 q_start, out, lse)
+    need = mla_verify_workspace_bytes(W, R, H, nseg)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _dev(workspace, None, "workspace")
+    _check(_lib.lib.mla_verify_attn_merge(
+        _ptr(q), _ptr(kv), num_blocks, block_size, page_size, _kv_dtype(kv), float(kv_scale),
+        float(sm_scale), _ptr(row_lens), _ptr(page_table), page_table.shape[2], _ptr(q_start),
+        q_start.shape[0] - 1, R, H, W, int(max_qlen), int(nseg), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def mla_verify_attn_merge_static(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen,
+                                 nseg, sm_scale, kv_scale=1.0, out, lse, stream=None):
+    """mla_verify_attn_merge with the partials in the library's static
+    scratch array (MLA_STATIC_SCRATCH_BYTES per GPU): the C call allocates
+    nothing, so out and lse must be passed. Calls that overlap on one GPU
+    race. Returns (out, lse)."""
+    R, H, W, num_blocks, block_size, out, lse = _attn_merge_args(q, kv, row_lens, page_table,
+                                                                 q_start, out, lse)
+    _check(_lib.lib.mla_verify_attn_merge_static(
+        _ptr(q), _ptr(kv), num_blocks, block_size, page_size, _kv_dtype(kv), float(kv_scale),
+        float(sm_scale), _ptr(row_lens), _ptr(page_table), page_table.shape[2], _ptr(q_start),
+        q_start.shape[0] - 1, R, H, W, int(max_qlen), int(nseg), _ptr(out), _ptr(lse),
+        _stream(stream)))
+    return out, lse
+
+
 def mla_shard_merge(shard_out, shard_lse, *, out=None, lse=None, stream=None):
     """Shard LSE merge of per-shard bf16 outputs [W,R,H,512] and natural-log
     LSEs [W,R,H]. Returns (out [R,H,512] bf16, lse [R,H] fp32)."""
@@ -408,6 +468,7 @@ def mla_verify_two_stage(dev, k_window, *, plan=None, stream=None):
 __all__ = [
     "mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes", "mla_verify_plan",
     "mla_verify_attn", "mla_lse_merge", "mla_verify_attn_shard", "mla_shard_merge",
+    "mla_verify_attn_merge", "mla_verify_attn_merge_static",
     "mla_last_error", "mla_verify_forward", "mla_verify_forward_shards",
     "mla_verify_two_stage", "mla_verify_two_stage_plan", "MlaError", "HEAD_DIM", "V_DIM",
 ]

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmla_verify.so")
 MLA_OK, MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 MLA_KV_BF16, MLA_KV_FP8_E4M3, MLA_KV_FP8_E5M2 = 0, 1, 2
 MLA_PLAN_ERR_QLEN, MLA_PLAN_ERR_BOUND, MLA_PLAN_ERR_BLOCKS, MLA_PLAN_ERR_ROWS = 1, 2, 4, 8
+MLA_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = {
     # name: (restype, argtypes)
@@ -42,6 +43,18 @@ EXPORTED = {
         ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "mla_verify_attn_merge": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "mla_verify_attn_merge_static": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
     "mla_shard_merge": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),

@@ -21,7 +21,7 @@ LIB_NAME = "libmla_verify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.hip", "attn_bf16.hip", "attn_fp8.hip", "merge.hip"]
+SOURCES = ["api.cpp", "plan.hip", "attn_bf16.hip", "attn_fp8.hip", "merge.hip", "scratch.hip"]
 
 # Packed fp32 instructions are switched off: hipcc -O3 would otherwise form
 # them from plain float code.

@@ -276,6 +276,107 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv, int64_t num_bl
                     "mla_verify_attn_shard launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of the one-call attention + merge; fills `a` but the partials.
+mla_status_t attn_merge_args(const char* fn, const void* q, const void* kv, int64_t num_blocks,
+                             int32_t block_size, int32_t page_size, mla_kv_dtype_t kv_dtype,
+                             float kv_scale, float sm_scale, const int32_t* row_lens,
+                             const int32_t* page_table, int32_t pt_width,
+                             const int32_t* q_start, int32_t N, int32_t R, int32_t H, int32_t W,
+                             int32_t max_qlen, int32_t nseg, void* out, float* lse,
+                             mla::AttnArgs& a, bool& fp8) {
+  const mla_status_t st = attn_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype,
+                                    kv_scale, sm_scale, row_lens, page_table, pt_width, q_start,
+                                    N, R, H, W, max_qlen, nseg, a, fp8);
+  if (st != MLA_OK) return st;
+  if (!out || !lse) return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+  if (!aligned16(out)) return fail(MLA_ERR_INVALID, "%s: out must be 16-byte aligned", fn);
+  return MLA_OK;
+}
+
+// Attention partials into `ws` (segm_out | segm_max | segm_expsum, the
+// layout of mla_verify_workspace_bytes) then the segment + shard merge.
+mla_status_t attn_merge_launch(const char* fn, mla::AttnArgs& a, bool fp8, unsigned char* ws,
+                               const int32_t* row_lens, const int32_t* q_start, int32_t page_size,
+                               void* out, float* lse, hipStream_t stream) {
+  const size_t cells = (size_t)a.W * (size_t)a.R * (size_t)a.H * (size_t)a.nseg;
+  a.segm_out = reinterpret_cast<float*>(ws);
+  a.segm_max = a.segm_out + cells * mla::kVDim;
+  a.segm_expsum = a.segm_max + cells;
+  const mla_status_t st = hip_status(mla::launch_attn(a, fp8, stream), fn);
+  if (st != MLA_OK) return st;
+  mla::MergeArgs m{};
+  m.segm_out = a.segm_out; m.segm_max = a.segm_max; m.segm_expsum = a.segm_expsum;
+  m.row_lens = row_lens; m.q_start = q_start; m.N = a.N; m.page_size = page_size;
+  m.R = a.R; m.H = a.H; m.W = a.W; m.nseg = a.nseg;
+  m.out = static_cast<uint16_t*>(out); m.lse = lse;
+  return hip_status(mla::launch_merge(m, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_verify_attn_merge(const void* q, const void* kv, int64_t num_blocks,
+                                   int32_t block_size, int32_t page_size,
+                                   mla_kv_dtype_t kv_dtype, float kv_scale, float sm_scale,
+                                   const int32_t* row_lens, const int32_t* page_table,
+                                   int32_t pt_width, const int32_t* q_start, int32_t N,
+                                   int32_t R, int32_t H, int32_t W, int32_t max_qlen,
+                                   int32_t nseg, void* workspace, size_t workspace_bytes,
+                                   void* out, float* lse, void* stream) {
+  const char* fn = "mla_verify_attn_merge";
+  mla::AttnArgs a;
+  bool fp8 = false;
+  const mla_status_t st =
+      attn_merge_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype, kv_scale,
+                      sm_scale, row_lens, page_table, pt_width, q_start, N, R, H, W, max_qlen,
+                      nseg, out, lse, a, fp8);
+  if (st != MLA_OK) return st;
+  const size_t need = mla_verify_workspace_bytes(W, R, H, nseg);
+  if (!workspace) return fail(MLA_ERR_INVALID, "%s: null workspace", fn);
+  if (!aligned16(workspace))
+    return fail(MLA_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INVALID, "%s: workspace of %zu bytes < %zu needed", fn,
+                workspace_bytes, need);
+  return attn_merge_launch(fn, a, fp8, static_cast<unsigned char*>(workspace), row_lens,
+                           q_start, page_size, out, lse, (hipStream_t)stream);
+}
+
+mla_status_t mla_verify_attn_merge_static(const void* q, const void* kv, int64_t num_blocks,
+                                          int32_t block_size, int32_t page_size,
+                                          mla_kv_dtype_t kv_dtype, float kv_scale,
+                                          float sm_scale, const int32_t* row_lens,
+                                          const int32_t* page_table, int32_t pt_width,
+                                          const int32_t* q_start, int32_t N, int32_t R,
+                                          int32_t H, int32_t W, int32_t max_qlen, int32_t nseg,
+                                          void* out, float* lse, void* stream) {
+  const char* fn = "mla_verify_attn_merge_static";
+  mla::AttnArgs a;
+  bool fp8 = false;
+  const mla_status_t st =
+      attn_merge_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype, kv_scale,
+                      sm_scale, row_lens, page_table, pt_width, q_start, N, R, H, W, max_qlen,
+                      nseg, out, lse, a, fp8);
+  if (st != MLA_OK) return st;
+  const size_t need = mla_verify_workspace_bytes(W, R, H, nseg);
+  if (need > MLA_STATIC_SCRATCH_BYTES)
+    return fail(MLA_ERR_INVALID,
+                "%s: the partials need %zu bytes, more than the %llu of the static scratch "
+                "array (use mla_verify_attn_merge with a workspace)",
+                fn, need, (unsigned long long)MLA_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = mla::static_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(MLA_ERR_HIP, "%s: static scratch address: %s", fn, hipGetErrorString(e));
+  return attn_merge_launch(fn, a, fp8, static_cast<unsigned char*>(ws), row_lens, q_start,
+                           page_size, out, lse, (hipStream_t)stream);
+}
+
 mla_status_t mla_lse_merge(const float* segm_out, const float* segm_max,
                            const float* segm_expsum, const int32_t* row_lens,
                            const int32_t* q_start, int32_t N, int32_t page_size, int32_t R,

@@ -82,6 +82,10 @@ struct ShardMergeArgs {
 // Largest W the shard merge takes (its per-wave LDS area).
 constexpr int kShardMergeMaxW = 1024;
 
+// Device address of the current device's static scratch array
+// (MLA_STATIC_SCRATCH_BYTES), looked up once per device.
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s);

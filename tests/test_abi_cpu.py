@@ -28,6 +28,7 @@ def test_header_declares_the_abi():
     assert names == sorted(["mla_subpage_size", "mla_pt_width", "mla_verify_workspace_bytes",
                             "mla_verify_plan", "mla_verify_two_stage_plan", "mla_verify_attn",
                             "mla_lse_merge", "mla_verify_attn_shard", "mla_shard_merge",
+                            "mla_verify_attn_merge", "mla_verify_attn_merge_static",
                             "mla_last_error"])
 
 
@@ -198,3 +199,46 @@ def _shard_merge(**over):
 def test_shard_merge_rejects_bad_arguments(over, code):
     assert _shard_merge(**over) == code
     assert "mla_shard_merge" in mla.mla_last_error()
+
+
+def _attn_merge(fn, **over):
+    a = dict(q=FAKE, kv=FAKE, num_blocks=8, block_size=16, page_size=16, kv_dtype=0,
+             kv_scale=1.0, sm_scale=0.04, row_lens=FAKE, page_table=FAKE, pt_width=4,
+             q_start=FAKE, N=1, R=1, H=16, W=1, max_qlen=1, nseg=1)
+    if fn == "mla_verify_attn_merge":
+        a.update(workspace=FAKE, workspace_bytes=1 << 20)
+    a.update(out=FAKE, lse=FAKE, stream=None)
+    a.update(over)
+    return getattr(_lib.lib, fn)(*a.values())
+
+
+@pytest.mark.parametrize("over,msg", [
+    (dict(workspace_bytes=100), "workspace of 100 bytes"),
+    (dict(workspace=None), "null workspace"),
+    (dict(workspace=FAKE + 4), "aligned"),
+    (dict(nseg=0), "nseg"),
+    (dict(out=None), "null"),
+])
+def test_attn_merge_rejects_bad_arguments(over, msg):
+    assert _attn_merge("mla_verify_attn_merge", **over) == _lib.MLA_ERR_INVALID
+    assert msg in mla.mla_last_error()
+
+
+def test_static_entry_rejects_sizes_beyond_its_scratch():
+    """The no-allocation entry point refuses, before any device call, a size
+    whose partials exceed the static array; one byte under the limit passes
+    the size check (and then fails on the fake pointers' other checks)."""
+    limit = _lib.MLA_STATIC_SCRATCH_BYTES
+    per_cell = (512 + 2) * 4
+    cells = limit // per_cell
+    H = 16
+    R = cells // H + 1                                   # W = nseg = 1: over the limit
+    assert mla.mla_verify_workspace_bytes(1, R, H, 1) > limit
+    assert _attn_merge("mla_verify_attn_merge_static", R=R, H=H) == _lib.MLA_ERR_INVALID
+    err = mla.mla_last_error()
+    assert "static scratch" in err and str(limit) in err
+    R_ok = cells // H
+    assert mla.mla_verify_workspace_bytes(1, R_ok, H, 1) <= limit
+    assert _attn_merge("mla_verify_attn_merge_static", R=R_ok, H=H, out=None) == \
+        _lib.MLA_ERR_INVALID
+    assert "null" in mla.mla_last_error()

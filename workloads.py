@@ -44,7 +44,7 @@ CONFIGS = {
     # batch 64, 12 heads, qlen 7, seq_len U[4096, 32768], fp8 KV, 4 shards
     # (split-K segments: the count measured fastest here; the config leaves it open)
     "fp8_verify_dcp4": dict(N=64, H=12, qlen=7, seq_range=(4096, 32768),
-                            block_size=64, W=4, kv_dtype="fp8_e4m3", nseg=4),
+                            block_size=64, W=4, kv_dtype="fp8_e4m3", nseg=2),
     # batch 16, 16 heads, qlen 4, seq_len 132000, 8 shards, 16 segments
     "long_context_dcp8": dict(N=16, H=16, qlen=4, seq_lens=[132000] * 16,
                               block_size=128, W=8, kv_dtype="bf16", nseg=16),

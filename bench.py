@@ -2,14 +2,13 @@
 """Throughput of the paged MLA verify hot path on one MI355X.
 
 One step = plan (row lengths + sub-page tables) -> attention -> merge, over
-one batch of the workload, inputs resident in HBM. With one segment per
-(request, shard) group (--path shards, the default then) the attention kernel
-folds the segment merge in and writes each shard's bf16 output + LSE, and the
-merge is the shard LSE merge alone; with split-K (--path split, the default
-for nseg > 1) the attention writes fp32 segment partials and the merge does
-the segment and the shard merge. The KV cache is rotated over several copies (more than the 256 MB
-Infinity Cache holds) so that no step re-reads the previous step's KV from
-cache. Timed steps launch the three calls from Python; --graph replays a HIP
+one batch of the workload, inputs resident in HBM. By default (--path shards)
+the attention kernel normalises every (shard, split-K segment) unit's result
+and writes it as bf16 output + natural-log LSE, and the merge is one LSE merge
+over the W * nseg units; --path split writes fp32 segment partials instead and
+merges them with the segment merge, then the shard merge. The KV cache is
+rotated over several copies (more than the 256 MB Infinity Cache holds) so
+that no step re-reads the previous step's KV from cache. Timed steps launch the three calls from Python; --graph replays a HIP
 graph of them instead (one graph per KV copy; on this stack a replay costs more
 launch overhead than the eager calls).
 `eager_split_us` splits eager steps with events (host launch gaps included);
@@ -44,9 +43,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="verify_dcp8")
     ap.add_argument("--nseg", type=int, default=None)
-    ap.add_argument("--path", choices=["auto", "split", "shards"], default="auto",
-                    help="split: attn partials -> lse_merge; shards: attn_shard -> "
-                         "shard_merge (nseg 1 only); auto: shards when nseg is 1")
+    ap.add_argument("--path", choices=["split", "shards"], default="shards",
+                    help="shards: attn_shard (every (shard, segment) unit normalised, bf16 "
+                         "+ LSE) -> shard_merge over the W * nseg units; split: attn fp32 "
+                         "partials -> lse_merge (segment merge, then shard merge)")
     ap.add_argument("--kv-copies", type=int, default=0,
                     help="KV copies to rotate over (0: enough for > 512 MB)")
     ap.add_argument("--graph", action="store_true",
@@ -161,9 +161,7 @@ def main():
 
     inp = wl.make_workload(args.workload, 0)
     nseg = inp["nseg"] if args.nseg is None else args.nseg
-    path = args.path if args.path != "auto" else ("shards" if nseg == 1 else "split")
-    if path == "shards" and nseg != 1:
-        raise SystemExit("--path shards needs nseg 1")
+    path = args.path
     dev = wl.to_device(inp)
     kv_bytes = wl.algorithmic_kv_bytes(inp)
     flops = wl.algorithmic_flops(inp)
@@ -184,8 +182,8 @@ def main():
         parts = (torch.empty((W, R, H, nseg, 512), **f32), torch.empty((W, R, H, nseg), **f32),
                  torch.empty((W, R, H, nseg), **f32))
     else:
-        parts = (torch.empty((W, R, H, 512), dtype=torch.bfloat16, device="cuda"),
-                 torch.empty((W, R, H), **f32))
+        parts = (torch.empty((W * nseg, R, H, 512), dtype=torch.bfloat16, device="cuda"),
+                 torch.empty((W * nseg, R, H), **f32))
 
     def attn(kv, row_lens, page_table, bufs):
         if path == "split":
@@ -197,7 +195,7 @@ def main():
             mla.mla_verify_attn_shard(dev["q"], kv, row_lens, page_table, dev["q_start"],
                                       page_size=page_size, max_qlen=dev["max_qlen"],
                                       sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
-                                      shard_out=bufs[0], shard_lse=bufs[1])
+                                      nseg=nseg, shard_out=bufs[0], shard_lse=bufs[1])
     out = torch.empty((R, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((R, H), **f32)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -287,7 +285,7 @@ def main():
     shard_us = None
     if W > 1:
         kv0 = [kv[0:1] for kv in kvs]
-        p0 = tuple(b[0:1] for b in parts)
+        p0 = tuple(b[0:nseg] if path == "shards" else b[0:1] for b in parts)
         rl0, pt0 = plan_bufs["row_lens"][0:1], plan_bufs["page_table"][0:1]
         attn0 = lambda k: attn(kv0[k % len(kv0)], rl0, pt0, p0)
         for k in range(3):
@@ -342,7 +340,7 @@ def main():
                           "kv_gbs_median": round(kv_bytes / (float(np.median(am)) * 1e-6) / 1e9, 1)},
         "shard0_alone_attn_us": None if shard_us is None else round(shard_us, 2),
         "bytes": {"kv_algorithmic": kv_bytes, "q": R * H * 1152, "out": R * H * (1024 + 4),
-                  "partials": W * R * H * (nseg * (2048 + 8) if path == "split" else 1024 + 4)},
+                  "partials": W * R * H * nseg * ((2048 + 8) if path == "split" else (1024 + 4))},
         "t_roof_us": round(max(kv_bytes / (HBM_PEAK_GBS * 1e9), flops / 2.5e15) * 1e6, 2),
         "hbm_copy_peak_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -241,23 +241,26 @@ mla_status_t mla_verify_attn(const void* q, const void* kv, int64_t num_blocks,
                              float* segm_expsum, void* stream);
 
 /*
- * One-segment attention with the segment merge folded in: for every shard,
- * row and head, the shard's normalised output and natural-log LSE over the
- * part of the row's window that the shard holds ([V51705] Implementation
- * breakdown item 4 with a single segment per (request, shard) group, whose
- * merge is the normalisation; [S34432] report: a DCP rank hands its peers
- * exactly this pair, bf16 output plus natural-log LSE). The same as
- * mla_verify_attn with nseg = 1 followed by the per-shard part of
- * mla_lse_merge, without the fp32 partials in between:
- *   o_r = O / e rounded to bf16,  lse_r = ln2 * (m2 + log2 e),
- * and o_r = 0, lse_r = -inf for a row with no token on shard r.
+ * Attention with each unit's result normalised, for the shard merge
+ * ([V51705] Implementation breakdown item 4: the split-K segments of a
+ * (request, shard) group; [S34432] report: a DCP rank hands its peers exactly
+ * this pair, bf16 output plus natural-log LSE). For every shard r, segment s,
+ * row and head, over the tokens of that segment of the row's window that the
+ * shard holds (the partition of mla_verify_attn):
+ *   o = O / e rounded to bf16,  lse = ln2 * (m2 + log2 e)
+ * (o = 0, lse = -inf without a token), written as source r * nseg + s. The
+ * LSE merge of all W * nseg sources (mla_shard_merge with W * nseg in place of
+ * W) gives the verify result: the segment merge and the shard merge of
+ * mla_lse_merge, done as one natural-log merge over (shard, segment) units,
+ * with each unit's output handed over as bf16. With nseg = 1 the source is
+ * the shard itself.
  *
  *   q, kv, num_blocks, block_size, page_size, kv_dtype, kv_scale, sm_scale,
- *   row_lens, page_table, pt_width, q_start, N, R, H, W, max_qlen:
+ *   row_lens, page_table, pt_width, q_start, N, R, H, W, max_qlen, nseg:
  *              as for mla_verify_attn (same checks, same error codes)
  * Outputs (device, caller-allocated):
- *   shard_out  [W, R, H, 512] bf16, 16-byte aligned
- *   shard_lse  [W, R, H] fp32
+ *   shard_out  [W * nseg, R, H, 512] bf16, 16-byte aligned
+ *   shard_lse  [W * nseg, R, H] fp32
  */
 mla_status_t mla_verify_attn_shard(const void* q, const void* kv,
                                    int64_t num_blocks, int32_t block_size,
@@ -267,8 +270,8 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv,
                                    const int32_t* page_table, int32_t pt_width,
                                    const int32_t* q_start, int32_t N, int32_t R,
                                    int32_t H, int32_t W, int32_t max_qlen,
-                                   void* shard_out, float* shard_lse,
-                                   void* stream);
+                                   int32_t nseg, void* shard_out,
+                                   float* shard_lse, void* stream);
 
 /*
  * Segment merge then shard merge ([V51705] merge snippet and Implementation
@@ -350,10 +353,14 @@ mla_status_t mla_verify_attn_merge_static(const void* q, const void* kv,
 
 /*
  * Shard merge alone ([V51705] Motivation: rank-local results combine through
- * the DCP attention merge; [S34432] review item 4: natural-log LSE):
+ * the DCP attention merge; [S34432] review item 4: natural-log LSE), over W
+ * sources (shards, or the W * nseg (shard, segment) sources of
+ * mla_verify_attn_shard):
  *   lse = ln sum_r exp(lse_r),  out = sum_r exp(lse_r - lse) * o_r  -> bf16,
- * shards with lse_r = -inf ignored; out = 0 and lse = -inf when every shard
- * is empty. Gives the same bits as the shard step of mla_lse_merge.
+ * sources with lse_r = -inf ignored (their o_r is not read); out = 0 and
+ * lse = -inf when every source is empty. With one source per shard it gives
+ * the same bits as the shard step of mla_lse_merge would for the same bf16
+ * per-shard outputs.
  *
  *   shard_out  [W, R, H, 512] bf16 (e.g. from mla_verify_attn_shard),
  *              16-byte aligned

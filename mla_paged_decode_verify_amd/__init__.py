@@ -164,11 +164,13 @@ def mla_verify_attn(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen
 
 
 def mla_verify_attn_shard(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen,
-                          sm_scale, kv_scale=1.0, shard_out=None, shard_lse=None,
+                          sm_scale, kv_scale=1.0, nseg=1, shard_out=None, shard_lse=None,
                           stream=None):
-    """One-segment attention with the segment merge folded in: per shard, row
-    and head the normalised bf16 output and natural-log LSE. Arguments as for
-    mla_verify_attn. Returns (shard_out [W,R,H,512] bf16, shard_lse [W,R,H])."""
+    """Attention with each (shard, segment) unit's result normalised: per
+    source r * nseg + s, row and head the bf16 output and natural-log LSE, for
+    mla_shard_merge over the W * nseg sources. Arguments as for
+    mla_verify_attn. Returns (shard_out [W*nseg,R,H,512] bf16,
+    shard_lse [W*nseg,R,H])."""
     _dev(q, torch.bfloat16, "q")
     _dev(kv, None, "kv")
     kvd = _kv_dtype(kv)
@@ -182,20 +184,21 @@ def mla_verify_attn_shard(q, kv, row_lens, page_table, q_start, *, page_size, ma
     if tuple(row_lens.shape) != (W, R) or page_table.shape[:2] != (W, R):
         raise ValueError("plan tensors do not match q / kv")
     N = q_start.shape[0] - 1
+    S = W * int(nseg)
     dev = q.device
     if shard_out is None:
-        shard_out = torch.empty((W, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+        shard_out = torch.empty((S, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
     if shard_lse is None:
-        shard_lse = torch.empty((W, R, H), dtype=torch.float32, device=dev)
+        shard_lse = torch.empty((S, R, H), dtype=torch.float32, device=dev)
     _dev(shard_out, torch.bfloat16, "shard_out")
     _dev(shard_lse, torch.float32, "shard_lse")
-    if shard_out.numel() != W * R * H * V_DIM or shard_lse.numel() != W * R * H:
+    if shard_out.numel() != S * R * H * V_DIM or shard_lse.numel() != S * R * H:
         raise ValueError("shard_out / shard_lse have the wrong size")
     _check(_lib.lib.mla_verify_attn_shard(
         _ptr(q), _ptr(kv), num_blocks, block_size, page_size, kvd, float(kv_scale),
         float(sm_scale), _ptr(row_lens), _ptr(page_table), page_table.shape[2],
-        _ptr(q_start), N, R, H, W, int(max_qlen), _ptr(shard_out), _ptr(shard_lse),
-        _stream(stream)))
+        _ptr(q_start), N, R, H, W, int(max_qlen), int(nseg), _ptr(shard_out),
+        _ptr(shard_lse), _stream(stream)))
     return shard_out, shard_lse
 
 
@@ -349,13 +352,12 @@ def mla_verify_forward(dev, *, nseg=1, plan=None, partials=None, out=None, lse=N
             "shard_lse": sl}
 
 
-def mla_verify_forward_shards(dev, *, plan=None, shards=None, out=None, lse=None,
+def mla_verify_forward_shards(dev, *, nseg=1, plan=None, shards=None, out=None, lse=None,
                               stream=None):
-    """plan -> one-segment attention (per-shard bf16 output + LSE) -> shard
-    merge, for the same dict as mla_verify_forward; the result equals
-    mla_verify_forward with nseg = 1. ``shards`` may pass (shard_out,
-    shard_lse) buffers. Returns a dict with the plan, shard_out, shard_lse,
-    out and lse."""
+    """plan -> attention with every (shard, segment) unit normalised (bf16
+    output + LSE) -> one LSE merge over the W * nseg units, for the same dict
+    as mla_verify_forward. ``shards`` may pass (shard_out, shard_lse) buffers.
+    Returns a dict with the plan, shard_out, shard_lse, out and lse."""
     if plan is None:
         plan = mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
                                dev["block_table"], dev["num_blocks"], dev["block_size"],
@@ -367,7 +369,7 @@ def mla_verify_forward_shards(dev, *, plan=None, shards=None, out=None, lse=None
     so, sl = mla_verify_attn_shard(dev["q"], dev["kv"], plan["row_lens"], plan["page_table"],
                                    dev["q_start"], page_size=plan["page_size"],
                                    max_qlen=dev["max_qlen"], sm_scale=dev["sm_scale"],
-                                   kv_scale=dev["kv_scale"], stream=stream, **kw)
+                                   kv_scale=dev["kv_scale"], nseg=nseg, stream=stream, **kw)
     o, l = mla_shard_merge(so, sl, out=out, lse=lse, stream=stream)
     return {"plan": plan, "shard_out": so, "shard_lse": sl, "out": o, "lse": l}
 

@@ -260,13 +260,14 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv, int64_t num_bl
                                    const int32_t* row_lens, const int32_t* page_table,
                                    int32_t pt_width, const int32_t* q_start, int32_t N,
                                    int32_t R, int32_t H, int32_t W, int32_t max_qlen,
-                                   void* shard_out, float* shard_lse, void* stream) {
+                                   int32_t nseg, void* shard_out, float* shard_lse,
+                                   void* stream) {
   const char* fn = "mla_verify_attn_shard";
   mla::AttnArgs a;
   bool fp8 = false;
   const mla_status_t st = attn_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype,
                                     kv_scale, sm_scale, row_lens, page_table, pt_width, q_start,
-                                    N, R, H, W, max_qlen, 1, a, fp8);
+                                    N, R, H, W, max_qlen, nseg, a, fp8);
   if (st != MLA_OK) return st;
   if (!shard_out || !shard_lse) return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
   if (!aligned16(shard_out))

@@ -532,18 +532,27 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// A unit with no token to read: in the one-segment form its rows still get
-// their (empty) shard results, o_r = 0 and lse_r = -inf; in the split form a
-// segment the merge reads gets the empty partials (maximum -inf, sum 0: the
-// merge then gives it weight 0 and never touches its output), and any other
+// Normalised form (a.shard_out set): every (shard, segment) unit is one
+// source of the LSE merge, source r * nseg + s; index of its (row qs of the
+// unit's request, head 0) in shard_out / shard_lse [W * nseg, R, H].
+__device__ __forceinline__ int64_t source_base(const AttnArgs& a, const WorkUnit& u) {
+  return ((int64_t)(u.r * a.nseg + u.s) * a.R + u.qs) * a.H;
+}
+
+// A unit with no token to read: in the normalised form its rows still get
+// their (empty) results, o = 0 and lse = -inf; in the split form a segment
+// the merge reads gets the empty partials (maximum -inf, sum 0: the merge
+// then gives it weight 0 and never touches its output), and any other
 // segment nothing.
 __device__ inline void store_empty(const AttnArgs& a, const WorkUnit& u, int wave, int lane) {
   const int64_t base = ((int64_t)u.r * a.R + u.qs) * a.H;
+  const int64_t sbase = source_base(a, u);
   for (int k = wave; k < kAttnRows && u.m0 + k < u.M; k += 4) {
     const int64_t e = base + u.m0 + k;
     if (a.shard_out != nullptr) {
-      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
-      if (lane == 0) a.shard_lse[e] = kNegInf;
+      const int64_t f = sbase + u.m0 + k;
+      *reinterpret_cast<uint4*>(a.shard_out + f * kVDim + 8 * lane) = make_uint4(0, 0, 0, 0);
+      if (lane == 0) a.shard_lse[f] = kNegInf;
     } else if (u.read && lane == 0) {
       a.segm_max[e * a.nseg + u.s] = kNegInf;
       a.segm_expsum[e * a.nseg + u.s] = 0.f;
@@ -564,9 +573,10 @@ __device__ inline void poison_uncovered(const AttnArgs& a, const WorkUnit& u, in
   for (int m = covered + wave; m < u.M; m += 4) {
     const int64_t e = base + m;
     if (a.shard_out != nullptr) {
-      *reinterpret_cast<uint4*>(a.shard_out + e * kVDim + 8 * lane) =
+      const int64_t f = source_base(a, u) + m;
+      *reinterpret_cast<uint4*>(a.shard_out + f * kVDim + 8 * lane) =
           make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-      if (lane == 0) reinterpret_cast<uint32_t*>(a.shard_lse)[e] = qnan;
+      if (lane == 0) reinterpret_cast<uint32_t*>(a.shard_lse)[f] = qnan;
     } else {
       const int64_t f = e * a.nseg + u.s;
       uint32_t* o = reinterpret_cast<uint32_t*>(a.segm_out + f * kVDim) + 8 * lane;
@@ -597,10 +607,11 @@ __device__ __forceinline__ void idle_tile(Issue&& issue) {
 // (maximum, sum and O relative to the maximum). O goes through LDS (`stage`:
 // this row group's 32 rows, a tile buffer no longer read) so that the global
 // stores write whole rows, 1 KB per instruction, instead of 16-byte pieces.
-// One-segment form (a.shard_out set): the segment merge of a single segment
-// is the normalisation, so the row's output O / sum goes out as bf16 with its
-// natural-log LSE ln2 (max + log2 sum), computed in the same operations and
-// order as the merge kernel would from the partials (same bits).
+// Normalised form (a.shard_out set): the merge of a single segment is the
+// normalisation, so the row's output O / sum goes out as bf16 with its
+// natural-log LSE ln2 (max + log2 sum) -- in the same fp32 operations and
+// order as the merge kernel applies to the partials -- as source
+// r * nseg + s of the LSE merge.
 constexpr int kStageRow = 4 * kVDim + 16;   // padded row of 512 fp32
 constexpr int kStageRowBf16 = 2 * kVDim + 16;  // padded row of 512 bf16
 static_assert(32 * kStageRow <= kBufBytes, "a row group's O fits a tile buffer");
@@ -627,7 +638,7 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
   const bool live = st.m_true != kNegInf && E > 0.f;
   if (row_ok && c == 0 && h == 0) {
     if (one_seg) {
-      a.shard_lse[((int64_t)u.r * a.R + u.qs) * a.H + mrow] =
+      a.shard_lse[source_base(a, u) + mrow] =
           live ? kLn2 * (st.m_true + __log2f(E)) : kNegInf;
     } else {
       const int64_t e = (((int64_t)u.r * a.R + u.qs) * a.H + mrow) * a.nseg + u.s;
@@ -660,7 +671,7 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       rows[k] = *reinterpret_cast<const uint4*>(stage + (16 * c + k) * kStageRowBf16 + 16 * lane);
-    const int64_t e0 = ((int64_t)u.r * a.R + u.qs) * a.H + row0;
+    const int64_t e0 = source_base(a, u) + row0;
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       if (row0 + k < u.M)

@@ -52,10 +52,11 @@ struct AttnArgs {
   float* segm_out;
   float* segm_max;
   float* segm_expsum;
-  // One-segment form (segm_* unused, nseg = 1): each row's shard output,
-  // normalised and rounded to bf16, and its natural-log LSE.
-  uint16_t* shard_out;       // [W, R, H, 512] bf16 bits, or null
-  float* shard_lse;          // [W, R, H]
+  // Normalised form (segm_* unused): each row's output over one (shard,
+  // segment) unit, normalised and rounded to bf16, and its natural-log LSE,
+  // as source r * nseg + s of the LSE merge.
+  uint16_t* shard_out;       // [W * nseg, R, H, 512] bf16 bits, or null
+  float* shard_lse;          // [W * nseg, R, H]
 };
 
 struct MergeArgs {

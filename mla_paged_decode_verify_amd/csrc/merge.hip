@@ -302,8 +302,9 @@ __global__ void __launch_bounds__(64 * kMergeWaves) merge_kernel(MergeArgs a) {
   store_out(a, pair, lane, res, lse_out);
 }
 
-// Shard merge alone, from per-shard bf16 outputs and natural-log LSEs: one
-// wave per (row, head) pair, each lane owning 8 latent dims. The weights are
+// Shard merge alone, from per-source bf16 outputs and natural-log LSEs (a
+// source is a shard, or one (shard, segment) unit of the normalised form):
+// one wave per (row, head) pair, each lane owning 8 latent dims. The weights are
 // formed exactly as in merge_kernel (largest LSE G, exp(lse_r - G), wave sum,
 // normalised), and the outputs are accumulated shard by shard in order, so
 // both kernels give the same bits for the same per-shard results.
@@ -389,10 +390,13 @@ __global__ void __launch_bounds__(64 * kMergeWaves) shard_merge_kernel(ShardMerg
   wave_lds_sync();
 
   for (int r0 = 0; r0 < W; r0 += 8) {
+    // sources without weight (lse -inf: no token of the row) are not read
     uint4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (r0 + j < W) v[j] = *reinterpret_cast<const uint4*>(src + (r0 + j) * rs * kVDim);
+      v[j] = (r0 + j < W && sw[r0 + j] != 0.f)
+                 ? *reinterpret_cast<const uint4*>(src + (r0 + j) * rs * kVDim)
+                 : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (r0 + j >= W) break;

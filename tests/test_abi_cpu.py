@@ -160,8 +160,8 @@ def test_python_binding_refuses_host_tensors():
 def _attn_shard(**over):
     a = dict(q=FAKE, kv=FAKE, num_blocks=8, block_size=16, page_size=16, kv_dtype=0,
              kv_scale=1.0, sm_scale=0.04, row_lens=FAKE, page_table=FAKE, pt_width=4,
-             q_start=FAKE, N=1, R=1, H=16, W=1, max_qlen=1, shard_out=FAKE, shard_lse=FAKE,
-             stream=None)
+             q_start=FAKE, N=1, R=1, H=16, W=1, max_qlen=1, nseg=1, shard_out=FAKE,
+             shard_lse=FAKE, stream=None)
     a.update(over)
     return _lib.lib.mla_verify_attn_shard(*a.values())
 
@@ -176,6 +176,7 @@ def _attn_shard(**over):
     (dict(shard_lse=None), _lib.MLA_ERR_INVALID),
     (dict(shard_out=FAKE + 8), _lib.MLA_ERR_INVALID),
     (dict(max_qlen=0), _lib.MLA_ERR_INVALID),
+    (dict(nseg=0), _lib.MLA_ERR_INVALID),
 ])
 def test_attn_shard_rejects_bad_arguments(over, code):
     assert _attn_shard(**over) == code

@@ -466,72 +466,89 @@ def test_two_stage_verify_matches_one_stage_and_oracle(W, I):
 
 # ------------------------------------------ one-segment (shard output) path ---
 
-def _run_shards(inp, poison=True):
+def _run_shards(inp, nseg=1, poison=True):
     """plan -> mla_verify_attn_shard -> mla_shard_merge, into buffers filled
     with NaN first, so that any element left unwritten fails."""
     dev = wl.to_device(inp)
-    W, R, H = inp["W"], inp["R"], inp["H"]
+    S, R, H = inp["W"] * nseg, inp["R"], inp["H"]
     fill = float("nan") if poison else 0.0
-    so = torch.full((W, R, H, 512), fill, dtype=torch.bfloat16, device="cuda")
-    sl = torch.full((W, R, H), fill, dtype=torch.float32, device="cuda")
+    so = torch.full((S, R, H, 512), fill, dtype=torch.bfloat16, device="cuda")
+    sl = torch.full((S, R, H), fill, dtype=torch.float32, device="cuda")
     out = torch.full((R, H, 512), fill, dtype=torch.bfloat16, device="cuda")
     lse = torch.full((R, H), fill, dtype=torch.float32, device="cuda")
-    res = mla.mla_verify_forward_shards(dev, shards=(so, sl), out=out, lse=lse)
+    res = mla.mla_verify_forward_shards(dev, nseg=nseg, shards=(so, sl), out=out, lse=lse)
     torch.cuda.synchronize()
     return {k: res[k].cpu() for k in ("shard_out", "shard_lse", "out", "lse")}
 
 
+def _oracle_sources(inp, plan, nseg):
+    """The oracle's normalised (shard, segment) sources: output, LSE and
+    weighted |v| of every source r * nseg + s (empty: 0, -inf, 0)."""
+    W, R, H = inp["W"], inp["R"], inp["H"]
+    _, _, _, parts = oracle_shard_results(inp, plan, nseg)
+    so = np.zeros((W * nseg, R, H, 512))
+    sa = np.zeros((W * nseg, R, H, 512))
+    sl = np.full((W * nseg, R, H), -np.inf)
+    for (i, r), (m2, e, Ov, act) in parts.items():
+        qs, Q = orc.request_rows(inp["q_start"], i)
+        for t in range(Q):
+            for s_ in np.nonzero(act[t])[0]:
+                src = r * nseg + s_
+                so[src, qs + t] = Ov[t, :, s_, :512] / e[t, :, s_, None]
+                sa[src, qs + t] = Ov[t, :, s_, 512:] / e[t, :, s_, None]
+                sl[src, qs + t] = orc.LN2 * (m2[t, :, s_] + np.log2(e[t, :, s_]))
+    return so, sl, sa
+
+
+@pytest.mark.parametrize("nseg", [1, 3])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_one_segment_path(name):
-    """The one-segment path (segment merge folded into the attention kernel,
-    then the shard merge alone) against the oracle's per-shard and final
-    results (each shard's output reaches the shard merge as bf16, so the
-    final bound includes that forced rounding); its per-shard results equal
-    those of plan -> attn (nseg 1) -> lse_merge bit for bit."""
+def test_one_segment_path(name, nseg):
+    """The normalised route (each (shard, segment) unit's output normalised
+    and handed over as bf16 with its LSE, then one LSE merge over the W * nseg
+    units) against the oracle's per-source and final results; its sources
+    equal what the split route's merge makes of the same partials (nseg 1:
+    bit for bit)."""
     spec = dict(SMALL[name])
     inp = wl.make_workload(spec, seed=1)
-    say(f"one-segment case {name} S={inp['seq_lens'].tolist()} Q={inp['qlens'].tolist()}")
-    got = _run_shards(inp)
+    say(f"normalised route case {name} nseg={nseg} S={inp['seq_lens'].tolist()} "
+        f"Q={inp['qlens'].tolist()}")
+    got = _run_shards(inp, nseg)
     ref_plan = oracle_plan(inp)
-    so, sl, sa, _ = oracle_shard_results(inp, ref_plan, 1, want_parts=False)
+    so, sl, sa = _oracle_sources(inp, ref_plan, nseg)
     g_so = got["shard_out"].float().numpy().astype(np.float64)
     g_sl = got["shard_lse"].numpy().astype(np.float64)
     assert not np.any(np.isnan(g_so)) and not np.any(np.isnan(g_sl))
-    check_out(g_so, so, inp["kv_dtype"], "shard_out", sa)
+    check_out(g_so, so, inp["kv_dtype"], "sources", sa)
     assert max_err(g_sl, sl) <= TOL_LSE
     out_ref, lse_ref = orc.verify_reference(inp)
     g_out = got["out"].float().numpy().astype(np.float64)
     assert np.all(np.isfinite(g_out)) and not np.any(np.isnan(got["lse"].numpy()))
     check_out(g_out, out_ref, inp["kv_dtype"], "out (bf16 hand-off)", weighted_abs_v(inp),
-              shard_ref=so, shard_lse_ref=sl, lse_ref=lse_ref, shard_absv=sa)
+              handoff=True)
     assert max_err(got["lse"].numpy(), lse_ref) <= TOL_LSE
-    # the split path with one segment computes the same per-shard bits (its
-    # merge then keeps them in fp32, so only its final output may differ)
-    split = run_gpu(inp, nseg=1, want_shards=True)
-    assert np.array_equal(g_so, split["shard_out"])
-    assert np.array_equal(g_sl, split["shard_lse"])
-    assert max_err(got["lse"].numpy(), split["lse"]) <= 1e-5
+    if nseg == 1:
+        # the split route with one segment computes the same per-shard bits
+        # (its merge then keeps them in fp32, so only its final output may differ)
+        split = run_gpu(inp, nseg=1, want_shards=True)
+        assert np.array_equal(g_so, split["shard_out"])
+        assert np.array_equal(g_sl, split["shard_lse"])
+        assert max_err(got["lse"].numpy(), split["lse"]) <= 1e-5
 
 
-@pytest.mark.parametrize("name", ["tiny_decode", "verify_dcp8"])
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
 def test_one_segment_path_named_workload(name):
-    """The one-segment path on the full-size workloads that run with one
-    segment, every request: per-shard and final out / lse against the
-    oracle."""
+    """The normalised route on the five full-size workloads (their own segment
+    counts), every request: out / lse against the oracle."""
     inp = named_workload(name)
-    got = _run_shards(inp)
+    got = _run_shards(inp, inp["nseg"])
     g_out = got["out"].float().numpy().astype(np.float64)
     g_lse = got["lse"].numpy().astype(np.float64)
     assert np.all(np.isfinite(g_out)) and np.all(np.isfinite(g_lse))
-    so, sl, sa, _ = oracle_shard_results(inp, oracle_plan(inp), 1, want_parts=False)
-    check_out(got["shard_out"].float().numpy(), so, "bf16", f"{name} shard_out", sa)
-    assert max_err(got["shard_lse"].numpy(), sl) <= TOL_LSE
     out_ref, lse_ref = orc.verify_reference(inp)
-    eo, _ = check_out(g_out, out_ref, "bf16", f"{name} out (bf16 hand-off)",
-                      weighted_abs_v(inp), shard_ref=so, shard_lse_ref=sl, lse_ref=lse_ref,
-                      shard_absv=sa)
+    eo, _ = check_out(g_out, out_ref, inp["kv_dtype"], f"{name} out (bf16 hand-off)",
+                      weighted_abs_v(inp), handoff=True)
     el = max_err(g_lse, lse_ref)
-    say(f"one-segment {name}: max|dout|={eo:.3e} max|dlse|={el:.3e}")
+    say(f"normalised route {name}: max|dout|={eo:.3e} max|dlse|={el:.3e}")
     assert el <= TOL_LSE
 
 

@@ -43,10 +43,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="verify_dcp8")
     ap.add_argument("--nseg", type=int, default=None)
-    ap.add_argument("--path", choices=["split", "shards"], default="shards",
+    ap.add_argument("--path", choices=["split", "shards", "persistent"], default="shards",
                     help="shards: attn_shard (every (shard, segment) unit normalised, bf16 "
                          "+ LSE) -> shard_merge over the W * nseg units; split: attn fp32 "
-                         "partials -> lse_merge (segment merge, then shard merge)")
+                         "partials -> lse_merge (segment merge, then shard merge); "
+                         "persistent: attn_persistent (one workgroup per compute unit on "
+                         "equal shares of all tiles, bf16 KV, one segment) -> shard_merge")
+    ap.add_argument("--ctas", type=int, default=0,
+                    help="persistent path: workgroups (0: one per compute unit)")
     ap.add_argument("--kv-copies", type=int, default=0,
                     help="KV copies to rotate over (0: enough for > 512 MB)")
     ap.add_argument("--graph", action="store_true",
@@ -61,62 +65,74 @@ def parse():
     return ap.parse_args()
 
 
-# sources of the attention kernel that runs a workload, by its KV dtype
+# sources of the attention kernel that runs a workload, by its KV dtype and path
 ATTN_SOURCES = {"bf16": ["attn_common.h", "attn_bf16.hip", "internal.h"],
-                "fp8": ["attn_common.h", "attn_fp8.hip", "internal.h"]}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_verify_dcp8_traffic.txt")
+                "fp8": ["attn_common.h", "attn_fp8.hip", "internal.h"],
+                "persistent": ["attn_common.h", "attn_persist.hip", "internal.h"]}
+ATTN_KERNELS = {"bf16": "attn_bf16_kernel", "fp8": "attn_fp8_kernel",
+                "persistent": "attn_persist_kernel"}
 
 
-def attn_source_hash(workload="verify_dcp8"):
-    """sha256 over the sources of the attention kernel that runs `workload`
-    (to tell whether stored counter readings still describe that kernel)."""
-    import hashlib
+def attn_kind(workload, path):
     import workloads as wl
-    kind = "bf16" if wl.CONFIGS[workload]["kv_dtype"] == "bf16" else "fp8"
+    if path == "persistent":
+        return "persistent"
+    return "bf16" if wl.CONFIGS[workload]["kv_dtype"] == "bf16" else "fp8"
+
+
+def attn_source_hash(workload="verify_dcp8", path="shards"):
+    """sha256 over the sources of the attention kernel that runs `workload`
+    on `path` (to tell whether stored counter readings still describe it)."""
+    import hashlib
     h = hashlib.sha256()
-    for name in ATTN_SOURCES[kind]:
+    for name in ATTN_SOURCES[attn_kind(workload, path)]:
         with open(os.path.join(ROOT, "mla_paged_decode_verify_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def stored_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None if there is none for this workload or the kernel changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
-    with open(TRAFFIC_FILE) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("workload") != workload or kv.get("source_sha256") != attn_source_hash(workload):
-        return None
-    try:
-        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+def summary_path(workload, path, what):
+    """profiles/ summary of `what` (traffic, mfma) for the kernel of `path`."""
+    stem = "attn_persist" if path == "persistent" else "attn"
+    return os.path.join(ROOT, "profiles", f"{stem}_{workload}_{what}.txt")
 
 
-def stored_mfma_flops(workload):
-    """Executed MFMA flops per attention launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
-    512) from the committed counter summary, or None if there is none for this
-    workload or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", f"attn_{workload}_mfma.txt")
-    if not os.path.exists(path):
+def _stored(workload, path, what):
+    """key: value lines of a committed counter summary, or None if there is
+    none for this workload and kernel or the kernel's sources changed since."""
+    fn = summary_path(workload, path, what)
+    if not os.path.exists(fn):
         return None
     kv = {}
-    with open(path) as f:
+    with open(fn) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.split("(")[0].strip()] = v.split()[0] if v.split() else ""
-    if kv.get("workload") != workload or kv.get("source_sha256") != attn_source_hash(workload):
+    if (kv.get("workload") != workload
+            or kv.get("source_sha256") != attn_source_hash(workload, path)
+            or kv.get("path", path) != path):
         return None
+    return kv
+
+
+def stored_traffic(workload, path="shards"):
+    """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, scaled) from
+    the committed counter summary, or None (none, or the kernel changed)."""
+    kv = _stored(workload, path, "traffic")
+    try:
+        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (TypeError, KeyError, ValueError):
+        return None
+
+
+def stored_mfma_flops(workload, path="shards"):
+    """Executed MFMA flops per attention launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
+    512) from the committed counter summary, or None."""
+    kv = _stored(workload, path, "mfma")
     try:
         return float(kv["executed_mfma_flops_per_launch"])
-    except (KeyError, ValueError):
+    except (TypeError, KeyError, ValueError):
         return None
 
 
@@ -178,6 +194,12 @@ def main():
                      page_table=torch.empty((W, R, ptw), **i32),
                      qo_indptr=torch.empty((R + 1,), **i32), err_flag=torch.zeros((1,), **i32))
     f32 = dict(dtype=torch.float32, device="cuda")
+    workspace = None
+    if path == "persistent":
+        if nseg != 1 or inp["kv_dtype"] != "bf16":
+            raise SystemExit("the persistent path takes bf16 KV and one segment")
+        workspace = torch.zeros(mla.mla_verify_attn_persistent_workspace_bytes(
+            inp["N"], W, H, dev["max_qlen"], args.ctas), dtype=torch.uint8, device="cuda")
     if path == "split":
         parts = (torch.empty((W, R, H, nseg, 512), **f32), torch.empty((W, R, H, nseg), **f32),
                  torch.empty((W, R, H, nseg), **f32))
@@ -191,6 +213,12 @@ def main():
                                 page_size=page_size, max_qlen=dev["max_qlen"], nseg=nseg,
                                 sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
                                 segm_out=bufs[0], segm_max=bufs[1], segm_expsum=bufs[2])
+        elif path == "persistent":
+            mla.mla_verify_attn_persistent(dev["q"], kv, row_lens, page_table, dev["q_start"],
+                                           page_size=page_size, max_qlen=dev["max_qlen"],
+                                           sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                                           ctas=args.ctas, workspace=workspace,
+                                           shard_out=bufs[0], shard_lse=bufs[1])
         else:
             mla.mla_verify_attn_shard(dev["q"], kv, row_lens, page_table, dev["q_start"],
                                       page_size=page_size, max_qlen=dev["max_qlen"],
@@ -285,7 +313,7 @@ def main():
     shard_us = None
     if W > 1:
         kv0 = [kv[0:1] for kv in kvs]
-        p0 = tuple(b[0:nseg] if path == "shards" else b[0:1] for b in parts)
+        p0 = tuple(b[0:nseg] if path != "split" else b[0:1] for b in parts)
         rl0, pt0 = plan_bufs["row_lens"][0:1], plan_bufs["page_table"][0:1]
         attn0 = lambda k: attn(kv0[k % len(kv0)], rl0, pt0, p0)
         for k in range(3):
@@ -314,7 +342,7 @@ def main():
     del cp, cq
     ms_step = wall * 1e3 / args.steps
     achieved = kv_bytes / (attn_launch_ms * 1e-3) / 1e9
-    mfma_flops = stored_mfma_flops(args.workload)
+    mfma_flops = stored_mfma_flops(args.workload, path)
     res = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -345,8 +373,8 @@ def main():
         "hbm_copy_peak_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(args.workload),
-                     "kernel": "attn_bf16_kernel" if inp["kv_dtype"] == "bf16" else "attn_fp8_kernel",
+                     "traffic": stored_traffic(args.workload, path),
+                     "kernel": ATTN_KERNELS[attn_kind(args.workload, path)],
                      "bytes_per_launch": kv_bytes, "flops_per_launch": flops,
                      "frac_of_copy_peak": round(achieved / copy_gbs, 4)},
         # the dense part: executed MFMA flops (from the committed counter

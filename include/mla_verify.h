@@ -274,6 +274,57 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv,
                                    float* shard_lse, void* stream);
 
 /*
+ * mla_verify_attn_shard with one segment, scheduled for balance ([V51011]
+ * Implementation breakdown item 3: the ASM decode path that vLLM routes to
+ * runs a persistent kernel on per-launch work metadata; the schedule here is
+ * this library's own). Same results layout and meaning as
+ * mla_verify_attn_shard(..., nseg = 1, ...): shard_out [W, R, H, 512] bf16
+ * and shard_lse [W, R, H], source r = shard r, for mla_shard_merge.
+ *
+ * All KV tiles of the launch -- every (request, 64-pair row block, shard)
+ * group's tiles in token order, groups in that order -- are one sequence of
+ * T tiles; `ctas` workgroups (one per compute unit) take contiguous ranges of
+ * floor(T/ctas) or ceil(T/ctas) tiles each, so every compute unit streams for
+ * about the same time whatever the spread of request lengths. A group that
+ * lies in one range is finished there; a group cut between ranges is
+ * finished by the piece that completes last, which combines all pieces'
+ * fp32 partial states (in piece order: the result does not depend on which
+ * piece comes last) and rounds once to bf16, like an uncut group. Each
+ * workgroup computes the schedule itself from row_lens and q_start; no extra
+ * launch and no host synchronisation.
+ *
+ *   q .. max_qlen: as for mla_verify_attn_shard; kv_dtype must be
+ *              MLA_KV_BF16 (fp8 caches: MLA_ERR_UNSUPPORTED)
+ *   ctas       workgroups, >= 1; 0 = the current device's compute-unit count
+ *   workspace  device, 256-byte aligned, at least
+ *              mla_verify_attn_persistent_workspace_bytes(N, W, H, max_qlen,
+ *              ctas) bytes: per-group arrival counters, then two partial-state
+ *              slots of 135168 bytes per workgroup. Its first
+ *              4 * N * W * ceil(max_qlen * H / 64) bytes (the counters) must
+ *              be zero before the first call; every completed call leaves them
+ *              zero again, so the same workspace serves later calls (and HIP
+ *              graph replays) without clearing. Calls that share a workspace
+ *              must not overlap.
+ *   shard_out, shard_lse: as for mla_verify_attn_shard with nseg = 1
+ * Limits: at most 2048 groups (N * W * ceil(max_qlen * H / 64)),
+ * pt_width * page_size < 2^30, groups times the tiles of the longest table
+ * row < 2^31 (MLA_ERR_UNSUPPORTED beyond; use mla_verify_attn_shard).
+ */
+size_t mla_verify_attn_persistent_workspace_bytes(int32_t N, int32_t W, int32_t H,
+                                                  int32_t max_qlen, int32_t ctas);
+mla_status_t mla_verify_attn_persistent(const void* q, const void* kv,
+                                        int64_t num_blocks, int32_t block_size,
+                                        int32_t page_size, mla_kv_dtype_t kv_dtype,
+                                        float kv_scale, float sm_scale,
+                                        const int32_t* row_lens,
+                                        const int32_t* page_table, int32_t pt_width,
+                                        const int32_t* q_start, int32_t N, int32_t R,
+                                        int32_t H, int32_t W, int32_t max_qlen,
+                                        int32_t ctas, void* workspace,
+                                        size_t workspace_bytes, void* shard_out,
+                                        float* shard_lse, void* stream);
+
+/*
  * Segment merge then shard merge ([V51705] merge snippet and Implementation
  * breakdown item 4; [S34432] review item 4 for the natural-log convention).
  * Per shard r, over its active segments (s*T*P < that row's length):

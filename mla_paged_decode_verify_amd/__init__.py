@@ -202,6 +202,57 @@ def mla_verify_attn_shard(q, kv, row_lens, page_table, q_start, *, page_size, ma
     return shard_out, shard_lse
 
 
+def mla_verify_attn_persistent_workspace_bytes(N: int, W: int, H: int, max_qlen: int,
+                                               ctas: int = 0) -> int:
+    return int(_lib.lib.mla_verify_attn_persistent_workspace_bytes(
+        int(N), int(W), int(H), int(max_qlen), int(ctas)))
+
+
+def mla_verify_attn_persistent(q, kv, row_lens, page_table, q_start, *, page_size, max_qlen,
+                               sm_scale, kv_scale=1.0, ctas=0, workspace=None, shard_out=None,
+                               shard_lse=None, stream=None):
+    """mla_verify_attn_shard with one segment, on the balanced persistent
+    schedule (ctas workgroups, 0 = one per compute unit). ``workspace``: a
+    uint8 device tensor of mla_verify_attn_persistent_workspace_bytes bytes
+    whose counters are zero (a new one is zero-filled here; every completed
+    call leaves it zeroed for the next). Returns (shard_out [W,R,H,512] bf16,
+    shard_lse [W,R,H])."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(kv, None, "kv")
+    kvd = _kv_dtype(kv)
+    _dev(row_lens, torch.int32, "row_lens")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(q_start, torch.int32, "q_start")
+    R, H, D = q.shape
+    W, num_blocks, block_size, D2 = kv.shape
+    if D != HEAD_DIM or D2 != HEAD_DIM:
+        raise ValueError("head dim must be 576")
+    if tuple(row_lens.shape) != (W, R) or page_table.shape[:2] != (W, R):
+        raise ValueError("plan tensors do not match q / kv")
+    N = q_start.shape[0] - 1
+    dev = q.device
+    if workspace is None:
+        nbytes = mla_verify_attn_persistent_workspace_bytes(N, W, H, max_qlen, ctas)
+        if nbytes == 0:
+            raise MlaError(_lib.MLA_ERR_INVALID, "persistent workspace size unavailable")
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    _dev(workspace, torch.uint8, "workspace")
+    if shard_out is None:
+        shard_out = torch.empty((W, R, H, V_DIM), dtype=torch.bfloat16, device=dev)
+    if shard_lse is None:
+        shard_lse = torch.empty((W, R, H), dtype=torch.float32, device=dev)
+    _dev(shard_out, torch.bfloat16, "shard_out")
+    _dev(shard_lse, torch.float32, "shard_lse")
+    if shard_out.numel() != W * R * H * V_DIM or shard_lse.numel() != W * R * H:
+        raise ValueError("shard_out / shard_lse have the wrong size")
+    _check(_lib.lib.mla_verify_attn_persistent(
+        _ptr(q), _ptr(kv), num_blocks, block_size, page_size, kvd, float(kv_scale),
+        float(sm_scale), _ptr(row_lens), _ptr(page_table), page_table.shape[2],
+        _ptr(q_start), N, R, H, W, int(max_qlen), int(ctas), _ptr(workspace),
+        workspace.numel(), _ptr(shard_out), _ptr(shard_lse), _stream(stream)))
+    return shard_out, shard_lse
+
+
 def _attn_merge_args(q, kv, row_lens, page_table, q_start, out, lse):
     _dev(q, torch.bfloat16, "q")
     _dev(kv, None, "kv")
@@ -353,10 +404,13 @@ def mla_verify_forward(dev, *, nseg=1, plan=None, partials=None, out=None, lse=N
 
 
 def mla_verify_forward_shards(dev, *, nseg=1, plan=None, shards=None, out=None, lse=None,
-                              stream=None):
+                              persistent=False, ctas=0, workspace=None, stream=None):
     """plan -> attention with every (shard, segment) unit normalised (bf16
     output + LSE) -> one LSE merge over the W * nseg units, for the same dict
     as mla_verify_forward. ``shards`` may pass (shard_out, shard_lse) buffers.
+    persistent: the attention runs on the balanced persistent schedule
+    (mla_verify_attn_persistent; nseg must be 1, bf16 KV), with ``ctas``
+    workgroups and an optional zeroed ``workspace``.
     Returns a dict with the plan, shard_out, shard_lse, out and lse."""
     if plan is None:
         plan = mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
@@ -366,10 +420,19 @@ def mla_verify_forward_shards(dev, *, nseg=1, plan=None, shards=None, out=None, 
     kw = {}
     if shards is not None:
         kw = dict(shard_out=shards[0], shard_lse=shards[1])
-    so, sl = mla_verify_attn_shard(dev["q"], dev["kv"], plan["row_lens"], plan["page_table"],
-                                   dev["q_start"], page_size=plan["page_size"],
-                                   max_qlen=dev["max_qlen"], sm_scale=dev["sm_scale"],
-                                   kv_scale=dev["kv_scale"], nseg=nseg, stream=stream, **kw)
+    if persistent:
+        if nseg != 1:
+            raise ValueError("the persistent schedule takes nseg = 1")
+        so, sl = mla_verify_attn_persistent(
+            dev["q"], dev["kv"], plan["row_lens"], plan["page_table"], dev["q_start"],
+            page_size=plan["page_size"], max_qlen=dev["max_qlen"], sm_scale=dev["sm_scale"],
+            kv_scale=dev["kv_scale"], ctas=ctas, workspace=workspace, stream=stream, **kw)
+    else:
+        so, sl = mla_verify_attn_shard(dev["q"], dev["kv"], plan["row_lens"],
+                                       plan["page_table"], dev["q_start"],
+                                       page_size=plan["page_size"], max_qlen=dev["max_qlen"],
+                                       sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                                       nseg=nseg, stream=stream, **kw)
     o, l = mla_shard_merge(so, sl, out=out, lse=lse, stream=stream)
     return {"plan": plan, "shard_out": so, "shard_lse": sl, "out": o, "lse": l}
 

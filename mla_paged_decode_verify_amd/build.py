@@ -21,7 +21,8 @@ LIB_NAME = "libmla_verify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.hip", "attn_bf16.hip", "attn_fp8.hip", "merge.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "plan.hip", "attn_bf16.hip", "attn_fp8.hip", "attn_persist.hip", "merge.hip",
+           "scratch.hip"]
 
 # Packed fp32 instructions are switched off: hipcc -O3 would otherwise form
 # them from plain float code.
@@ -30,7 +31,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # accumulators in VGPRs (they rescale them with plain VALU multiplies; AGPR
 # copies would cost 256 moves a tile) and the query fragments in AGPRs.
 _ATTN = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
-SOURCE_FLAGS = {"attn_bf16.hip": _ATTN, "attn_fp8.hip": _ATTN}
+SOURCE_FLAGS = {"attn_bf16.hip": _ATTN, "attn_fp8.hip": _ATTN, "attn_persist.hip": _ATTN}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 

@@ -277,6 +277,86 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv, int64_t num_bl
                     "mla_verify_attn_shard launch");
 }
 
+namespace {
+
+// Groups of the persistent schedule, and the byte size of its counters
+// (padded so that the slots start 256-byte aligned).
+int64_t persist_groups(int32_t N, int32_t W, int32_t H, int32_t max_qlen) {
+  const int64_t mblocks = ((int64_t)max_qlen * H + mla::kAttnRows - 1) / mla::kAttnRows;
+  return (int64_t)N * W * mblocks;
+}
+size_t persist_counter_bytes(int64_t groups) { return ((size_t)groups * 4 + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t mla_verify_attn_persistent_workspace_bytes(int32_t N, int32_t W, int32_t H,
+                                                  int32_t max_qlen, int32_t ctas) {
+  if (N < 1 || W < 1 || H < 1 || max_qlen < 1 || ctas < 0) return 0;
+  if (ctas == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      return 0;
+    ctas = cus;
+  }
+  return persist_counter_bytes(persist_groups(N, W, H, max_qlen)) +
+         (size_t)2 * (size_t)ctas * mla::kPersistSlotBytes;
+}
+
+mla_status_t mla_verify_attn_persistent(const void* q, const void* kv, int64_t num_blocks,
+                                        int32_t block_size, int32_t page_size,
+                                        mla_kv_dtype_t kv_dtype, float kv_scale, float sm_scale,
+                                        const int32_t* row_lens, const int32_t* page_table,
+                                        int32_t pt_width, const int32_t* q_start, int32_t N,
+                                        int32_t R, int32_t H, int32_t W, int32_t max_qlen,
+                                        int32_t ctas, void* workspace, size_t workspace_bytes,
+                                        void* shard_out, float* shard_lse, void* stream) {
+  const char* fn = "mla_verify_attn_persistent";
+  mla::AttnArgs a;
+  bool fp8 = false;
+  const mla_status_t st = attn_args(fn, q, kv, num_blocks, block_size, page_size, kv_dtype,
+                                    kv_scale, sm_scale, row_lens, page_table, pt_width, q_start,
+                                    N, R, H, W, max_qlen, 1, a, fp8);
+  if (st != MLA_OK) return st;
+  if (fp8) return fail(MLA_ERR_UNSUPPORTED, "%s: bf16 KV caches only", fn);
+  if (!shard_out || !shard_lse || !workspace)
+    return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
+  if (!aligned16(shard_out))
+    return fail(MLA_ERR_INVALID, "%s: shard_out must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLA_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+  if (ctas < 0 || ctas > 65536)
+    return fail(MLA_ERR_INVALID, "%s: ctas must be 0 .. 65536 (got %d)", fn, ctas);
+  const int64_t groups = persist_groups(N, W, H, max_qlen);
+  const int64_t tiles_per_row = ((int64_t)pt_width * page_size + 63) / 64;
+  if (groups > mla::kPersistMaxGroups)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: %lld groups (N * W * row blocks) > %d", fn,
+                (long long)groups, mla::kPersistMaxGroups);
+  if ((int64_t)pt_width * page_size >= (1LL << 30) || groups * tiles_per_row >= (1LL << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: too many tiles for the schedule", fn);
+  if (ctas == 0) {
+    int dev = 0, cus = 0;
+    const hipError_t e1 = hipGetDevice(&dev);
+    if (e1 != hipSuccess) return hip_status(e1, fn);
+    const hipError_t e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e2 != hipSuccess) return hip_status(e2, fn);
+    ctas = cus > 0 ? cus : 1;
+  }
+  const size_t need = persist_counter_bytes(groups) + (size_t)2 * ctas * mla::kPersistSlotBytes;
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INVALID, "%s: workspace of %zu bytes < %zu needed", fn, workspace_bytes,
+                need);
+  a.shard_out = static_cast<uint16_t*>(shard_out);
+  a.shard_lse = shard_lse;
+  mla::PersistArgs p{};
+  p.counters = static_cast<int32_t*>(workspace);
+  p.slots = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                     persist_counter_bytes(groups));
+  p.ctas = ctas;
+  return hip_status(mla::launch_attn_persist(a, p, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"
 
 namespace {

@@ -17,14 +17,6 @@
 namespace mla {
 namespace {
 
-// Slice pages of 64 consecutive tiles for one wave: lane j holds the sub-page
-// of tokens tb0 + 64 j + 16 w .. +15 (the last in-range entry past the
-// segment end; tokens there are masked and read from the zero row).
-__device__ __forceinline__ int32_t slice_pages(const AttnArgs& a, const int32_t* pt_row, int tb0,
-                                               int hi, int wave, int lane) {
-  const int64_t tok = min((int64_t)tb0 + (int64_t)kTile * lane + 16 * wave, (int64_t)hi - 1);
-  return pt_row[tok >> a.page_shift];
-}
 
 template <bool SLICE>
 __global__ void __launch_bounds__(kThreads, 1) attn_bf16_kernel(AttnArgs a) {

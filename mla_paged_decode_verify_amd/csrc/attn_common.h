@@ -190,6 +190,15 @@ __device__ __forceinline__ void issue_slice(const SliceSrc& v, const unsigned ch
   }
 }
 
+// Slice pages of 64 consecutive tiles for one wave: lane j holds the sub-page
+// of tokens tb0 + 64 j + 16 w .. +15 (the last in-range entry past the
+// segment end; tokens there are masked and read from the zero row).
+__device__ __forceinline__ int32_t slice_pages(const AttnArgs& a, const int32_t* pt_row, int tb0,
+                                               int hi, int wave, int lane) {
+  const int64_t tok = min((int64_t)tb0 + (int64_t)kTile * lane + 16 * wave, (int64_t)hi - 1);
+  return pt_row[tok >> a.page_shift];
+}
+
 // Work unit of a workgroup and the segment [lo, hi) of local tokens it covers
 // (valid: the request's rows are well formed and the row block exists).
 struct WorkUnit {
@@ -615,10 +624,19 @@ __device__ __forceinline__ void idle_tile(Issue&& issue) {
 constexpr int kStageRow = 4 * kVDim + 16;   // padded row of 512 fp32
 constexpr int kStageRowBf16 = 2 * kVDim + 16;  // padded row of 512 bf16
 static_assert(32 * kStageRow <= kBufBytes, "a row group's O fits a tile buffer");
+// kLdsOnly: the barriers order LDS traffic only, for a caller that keeps
+// global loads in flight across the epilogue (normalised form only).
+template <bool kLdsOnly = false>
 __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit& u,
                                                const WaveState& st, RowExchange& rx,
                                                unsigned char* stage, int mrow, bool row_ok, int g,
                                                int c, int lane) {
+  auto barrier = [] {
+    if constexpr (kLdsOnly)
+      lds_barrier();
+    else
+      __syncthreads();
+  };
   const int h = lane >> 5;
   const int n32 = lane & 31;
   float l_row;
@@ -628,7 +646,7 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
     l_row = __uint_as_float(q[0]) + __uint_as_float(q[1]);
   }
   if (h == 0) rx.l[g][c][n32] = l_row;
-  __syncthreads();                          // also: no wave reads a tile buffer any more
+  barrier();                                // also: no wave reads a tile buffer any more
   const float L = l_row + rx.l[g][c ^ 1][n32];
   // move O and l from the reference exponent to the true maximum
   float fix = 1.f;
@@ -662,7 +680,7 @@ __device__ __forceinline__ void store_partials(const AttnArgs& a, const WorkUnit
             make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
       }
     }
-    __syncthreads();
+    barrier();
     // wave (g, c) stores rows 16c .. 16c + 15 of its row group: one 1 KB
     // row of bf16 per instruction, 8 dims per lane
     // (all 16 LDS reads first, then the stores: one LDS round trip, not 16)

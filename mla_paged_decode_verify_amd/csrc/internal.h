@@ -80,6 +80,19 @@ struct ShardMergeArgs {
   float* lse;
 };
 
+// Workspace of the balanced persistent attention kernel.
+struct PersistArgs {
+  int32_t* counters;         // [groups]: arrivals per cut group, zero between calls
+  float* slots;              // [2 * ctas] partial states of cut groups' pieces
+  int32_t ctas;              // workgroups (one per compute unit)
+};
+// Limit of the persistent kernel's in-kernel schedule: groups (request, row
+// block, shard) per launch.
+constexpr int kPersistMaxGroups = 2048;
+// One piece's partial state: per wave and lane 32 float4 of O and one of
+// (reference exponent, running maximum, sum).
+constexpr size_t kPersistSlotBytes = (size_t)4 * 33 * 64 * 16;
+
 // Largest W the shard merge takes (its per-wave LDS area).
 constexpr int kShardMergeMaxW = 1024;
 
@@ -90,6 +103,7 @@ hipError_t static_scratch(void** ptr);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_persist(const AttnArgs& a, const PersistArgs& p, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 

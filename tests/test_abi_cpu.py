@@ -29,7 +29,8 @@ def test_header_declares_the_abi():
                             "mla_verify_plan", "mla_verify_two_stage_plan", "mla_verify_attn",
                             "mla_lse_merge", "mla_verify_attn_shard", "mla_shard_merge",
                             "mla_verify_attn_merge", "mla_verify_attn_merge_static",
-                            "mla_last_error"])
+                            "mla_verify_attn_persistent",
+                            "mla_verify_attn_persistent_workspace_bytes", "mla_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -243,3 +244,41 @@ def test_static_entry_rejects_sizes_beyond_its_scratch():
     assert _attn_merge("mla_verify_attn_merge_static", R=R_ok, H=H, out=None) == \
         _lib.MLA_ERR_INVALID
     assert "null" in mla.mla_last_error()
+
+
+def _attn_persistent(**over):
+    a = dict(q=FAKE, kv=FAKE, num_blocks=8, block_size=16, page_size=16, kv_dtype=0,
+             kv_scale=1.0, sm_scale=0.04, row_lens=FAKE, page_table=FAKE, pt_width=4,
+             q_start=FAKE, N=1, R=1, H=16, W=1, max_qlen=1, ctas=256, workspace=FAKE,
+             workspace_bytes=1 << 30, shard_out=FAKE, shard_lse=FAKE, stream=None)
+    a.update(over)
+    return _lib.lib.mla_verify_attn_persistent(*a.values())
+
+
+def test_persistent_workspace_bytes():
+    """Counters (4 bytes per group, padded to 256) then two 135168-byte
+    partial-state slots per workgroup."""
+    ws = mla.mla_verify_attn_persistent_workspace_bytes
+    assert ws(32, 8, 16, 4, 256) == 1024 + 2 * 256 * 135168     # 256 groups
+    assert ws(3, 3, 12, 7, 8) == 256 + 2 * 8 * 135168            # 18 groups
+    assert ws(0, 8, 16, 4, 256) == 0 and ws(1, 1, 1, 1, -1) == 0
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(kv_dtype=1), _lib.MLA_ERR_UNSUPPORTED, "bf16"),
+    (dict(workspace=None), _lib.MLA_ERR_INVALID, "null"),
+    (dict(workspace=FAKE + 16), _lib.MLA_ERR_INVALID, "256-byte"),
+    (dict(workspace_bytes=1000), _lib.MLA_ERR_INVALID, "workspace of 1000 bytes"),
+    (dict(ctas=-1), _lib.MLA_ERR_INVALID, "ctas"),
+    (dict(N=2049), _lib.MLA_ERR_UNSUPPORTED, "groups"),
+    (dict(pt_width=1 << 26), _lib.MLA_ERR_UNSUPPORTED, "tiles"),
+    (dict(shard_out=FAKE + 8), _lib.MLA_ERR_INVALID, "aligned"),
+    (dict(max_qlen=0), _lib.MLA_ERR_INVALID, "max_qlen"),
+])
+def test_persistent_rejects_bad_arguments(over, code, msg):
+    """Every check runs before any device call (these are host pointers that
+    are never dereferenced)."""
+    assert _attn_persistent(**over) == code
+    err = mla.mla_last_error()
+    assert "mla_verify_attn_persistent" in err and msg in err
+

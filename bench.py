@@ -2,15 +2,19 @@
 """Throughput of the paged MLA verify hot path on one MI355X.
 
 One step = plan (row lengths + sub-page tables) -> attention -> merge, over
-one batch of the workload, inputs resident in HBM. By default (--path shards)
-the attention kernel normalises every (shard, split-K segment) unit's result
-and writes it as bf16 output + natural-log LSE, and the merge is one LSE merge
-over the W * nseg units; --path split writes fp32 segment partials instead and
-merges them with the segment merge, then the shard merge. The KV cache is
+one batch of the workload, inputs resident in HBM. Routes (--path; by default
+the workload's own, measured fastest): shards -- the attention kernel runs one
+workgroup per (shard, split-K segment, row block) unit, normalises each unit's
+result and writes it as bf16 output + natural-log LSE, and the merge is one
+LSE merge over the W * nseg units; persistent -- one workgroup per compute
+unit on equal shares of all tiles (bf16 KV; groups cut between workgroups are
+combined in the kernel), then the LSE merge over the W shards; split -- fp32
+segment partials, then the segment merge and the shard merge. The KV cache is
 rotated over several copies (more than the 256 MB Infinity Cache holds) so
-that no step re-reads the previous step's KV from cache. Timed steps launch the three calls from Python; --graph replays a HIP
-graph of them instead (one graph per KV copy; on this stack a replay costs more
-launch overhead than the eager calls).
+that no step re-reads the previous step's KV from cache. Timed steps launch
+the three calls from Python; --graph replays a HIP graph of them instead (one
+graph per KV copy; on this stack a replay costs more launch overhead than the
+eager calls).
 `eager_split_us` splits eager steps with events (host launch gaps included);
 the attention kernel's own duration comes from back-to-back launches.
 Prints one JSON line.
@@ -43,8 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="verify_dcp8")
     ap.add_argument("--nseg", type=int, default=None)
-    ap.add_argument("--path", choices=["split", "shards", "persistent"], default="shards",
-                    help="shards: attn_shard (every (shard, segment) unit normalised, bf16 "
+    ap.add_argument("--path", choices=["split", "shards", "persistent"], default=None,
+                    help="default: the workload's route (persistent for long_context_dcp8 "
+                         "and ragged_mixed, shards otherwise). shards: attn_shard (every (shard, segment) unit normalised, bf16 "
                          "+ LSE) -> shard_merge over the W * nseg units; split: attn fp32 "
                          "partials -> lse_merge (segment merge, then shard merge); "
                          "persistent: attn_persistent (one workgroup per compute unit on "
@@ -57,6 +62,9 @@ def parse():
                     help="replay a HIP graph of each step's three launches instead of "
                          "launching them from Python")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shard0", action="store_true",
+                    help="skip the shard-0-alone timing (every attention launch of the run "
+                         "is then a full one, for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="before the timed steps, run a plain elementwise copy of MB MiB "
@@ -176,8 +184,8 @@ def main():
     import mla_paged_decode_verify_amd as mla
 
     inp = wl.make_workload(args.workload, 0)
-    nseg = inp["nseg"] if args.nseg is None else args.nseg
-    path = args.path
+    path = args.path or inp["path"]
+    nseg = (1 if path == "persistent" else inp["nseg"]) if args.nseg is None else args.nseg
     dev = wl.to_device(inp)
     kv_bytes = wl.algorithmic_kv_bytes(inp)
     flops = wl.algorithmic_flops(inp)
@@ -311,7 +319,7 @@ def main():
     # One GPU's share in a real DCP deployment: shard 0 alone at its real
     # shape (its pool, its row lengths and page table), back to back.
     shard_us = None
-    if W > 1:
+    if W > 1 and not args.no_shard0:
         kv0 = [kv[0:1] for kv in kvs]
         p0 = tuple(b[0:nseg] if path != "split" else b[0:1] for b in parts)
         rl0, pt0 = plan_bufs["row_lens"][0:1], plan_bufs["page_table"][0:1]

@@ -187,3 +187,67 @@ def test_graph_one_segment_route_replays_new_lengths():
         assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
         assert torch.equal(shards[0], split["shard_out"])
         assert torch.equal(shards[1], split["shard_lse"])
+
+
+@pytest.mark.parametrize("ctas", [0, 7])
+def test_graph_persistent_route_replays_new_lengths(ctas):
+    """The persistent route (plan -> attn_persistent -> shard_merge) captured
+    once with one workspace: its arrival counters are left at zero by every
+    launch, so each replay -- lengths changed in place before it, some groups
+    cut between workgroups, some shards empty -- equals an eager run of the
+    same route on the new lengths bit for bit."""
+    spec = small_spec(N=6, W=4, qlen=3, seq_range=(100, 1500), nseg=1)
+    inp = wl.make_workload(spec, seed=21)
+    dev = wl.to_device(inp)
+    nbytes = mla.mla_verify_attn_persistent_workspace_bytes(inp["N"], inp["W"], inp["H"],
+                                                            dev["max_qlen"], ctas)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    first = mla.mla_verify_forward_shards(dev, persistent=True, ctas=ctas, workspace=ws)
+    torch.cuda.synchronize()
+    plan_bufs = {k: torch.empty_like(first["plan"][k])
+                 for k in ("row_lens", "page_table", "qo_indptr")}
+    plan_bufs["err_flag"] = torch.zeros_like(first["plan"]["err_flag"])
+    shards = (torch.empty_like(first["shard_out"]), torch.empty_like(first["shard_lse"]))
+    out, lse = torch.empty_like(first["out"]), torch.empty_like(first["lse"])
+
+    def step():
+        plan = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
+                                   dev["block_table"], dev["num_blocks"], dev["block_size"],
+                                   dev["max_kv_seq_len"], **plan_bufs)
+        mla.mla_verify_forward_shards(dev, plan=plan, shards=shards, out=out, lse=lse,
+                                      persistent=True, ctas=ctas, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    ws2 = torch.zeros_like(ws)
+    rng = np.random.default_rng(8)
+    S0, Q = inp["seq_lens"].copy(), inp["qlens"]
+    for rep in range(4):
+        S = np.array([int(rng.integers(q, s + 1)) for q, s in zip(Q, S0)], dtype=np.int64)
+        if rep == 2:
+            S[:2] = Q[:2]
+        say(f"  replay {rep}: S={S.tolist()}")
+        dev["seq_lens"].copy_(torch.from_numpy(S.astype(np.int32)).to("cuda"))
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        for b in shards:
+            b.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = mla.mla_verify_forward_shards(dev, persistent=True, ctas=ctas, workspace=ws2)
+        torch.cuda.synchronize()
+        assert int(plan_bufs["err_flag"].item()) == 0
+        assert torch.equal(shards[0], ref["shard_out"]) and torch.equal(shards[1], ref["shard_lse"])
+        assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
+        groups = inp["N"] * inp["W"] * (-(-dev["max_qlen"] * inp["H"] // 64))
+        assert int(ws[:4 * groups].view(torch.int32).abs().sum().item()) == 0

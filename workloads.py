@@ -46,13 +46,18 @@ CONFIGS = {
     "fp8_verify_dcp4": dict(N=64, H=12, qlen=7, seq_range=(4096, 32768),
                             block_size=64, W=4, kv_dtype="fp8_e4m3", nseg=2),
     # batch 16, 16 heads, qlen 4, seq_len 132000, 8 shards, 16 segments
+    # (nseg: the pages' split for the unit-per-workgroup kernel; "path": the
+    # route measured fastest, the persistent kernel, whose balanced schedule
+    # replaces the fixed split)
     "long_context_dcp8": dict(N=16, H=16, qlen=4, seq_lens=[132000] * 16,
-                              block_size=128, W=8, kv_dtype="bf16", nseg=16),
+                              block_size=128, W=8, kv_dtype="bf16", nseg=16,
+                              path="persistent"),
     # 128 requests, 128 heads, qlen U{1..8}, seq_len log-U[256, 65536]
-    # (split-K segments: the count measured fastest here; the config leaves it open)
+    # (split-K segments: the count measured fastest for the unit-per-workgroup
+    # kernel; the config leaves it open. "path" as above)
     "ragged_mixed": dict(N=128, H=128, qlen_range=(1, 8),
                          seq_log_range=(256, 65536), block_size=256, W=1,
-                         kv_dtype="bf16", nseg=4),
+                         kv_dtype="bf16", nseg=4, path="persistent"),
 }
 CONFIG_ORDER = ["tiny_decode", "verify_dcp8", "fp8_verify_dcp4",
                 "long_context_dcp8", "ragged_mixed"]
@@ -173,6 +178,7 @@ def make_workload(spec, seed: int = 0, *, q_mode: str = "normal",
         "interleave": I,
         "kv_dtype": kv_dtype, "kv_scale": float(kv_scale),
         "sm_scale": float(sm_scale), "nseg": int(spec.get("nseg", 1)),
+        "path": spec.get("path", "shards"),
         "seq_lens": seq_lens, "qlens": qlens, "q_start": q_start, "R": R,
         "block_table": block_table, "num_blocks": num_blocks,
         "max_kv_seq_len": int(local_max.max()),

@@ -13,18 +13,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_traffic_summary_parses():
-    # the stored HBM traffic belongs to the verify workload; other workloads get None
+    # a stored HBM traffic figure belongs to one workload and one kernel: a
+    # kernel without a summary (or whose sources changed since) gets None
     t = bench.stored_traffic("verify_dcp8")
     assert t is None or t > 0
-    assert bench.stored_traffic("ragged_mixed") is None
+    t = bench.stored_traffic("long_context_dcp8", "persistent")
+    assert t is None or t > 0
+    assert bench.stored_traffic("verify_dcp8", "split") is None
+    assert bench.stored_traffic("no_such_workload") is None
 
 
 def test_mfma_summaries_parse_and_agree_with_instruction_count():
-    for wl in ("verify_dcp8", "ragged_mixed"):
-        path = os.path.join(ROOT, "profiles", f"attn_{wl}_mfma.txt")
-        if not os.path.exists(path):
+    for wl, route in (("verify_dcp8", "shards"), ("ragged_mixed", "persistent"),
+                      ("long_context_dcp8", "persistent")):
+        if not os.path.exists(bench.summary_path(wl, route, "mfma")):
             continue
-        f = bench.stored_mfma_flops(wl)
+        f = bench.stored_mfma_flops(wl, route)
         if f is None:              # summary taken before the kernel last changed
             continue
         # every v_mfma_f32_32x32x16_bf16 is 32768 flops: the executed count is a

@@ -15,10 +15,14 @@
 // One workgroup = 4 waves = one work unit (request i, shard r, segment s,
 // 64-row block of the request's Q_i*H (row, head) pairs). All rows of a
 // request share the shard's KV, so a KV tile is read from HBM once per block.
-// LDS tile layout (64 tokens): latent [64][512 bf16 + 16 pad] -- with this row
-// stride neither the K-fragment reads nor the transposed V reads hit bank
-// conflicts (measured with SQ_LDS_BANK_CONFLICT) -- and rope [64][8 chunks of
-// 16 B] with chunk c of token t in slot c ^ (t & 7).
+// LDS tile layout (64 tokens): latent rows of 512 bf16 in 1056-byte slots,
+// row r starting 16 bytes into its slot when bit 3 of r is set, and rope
+// [64][8 chunks of 16 B] with chunk c of token t in slot c ^ ((t >> 1) & 7).
+// So the 16 rows that a K-fragment read touches at once (16 bytes each) fall
+// on 16 different groups of 4 banks -- 1056-byte rows alone map rows r and
+// r + 8 to the same banks -- and the same holds for the rope chunks; the
+// offsets are per row, so a lane's fragment addresses stay one base plus
+// constants.
 #pragma once
 
 #include "internal.h"
@@ -49,10 +53,13 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;       // log2 units
 constexpr float kLn2 = 0.693147180559945309f;
 
-// Slot permutation of the 16-byte chunks of latent row r.
-__device__ __forceinline__ int lat_swz(int r) { return 0; }
-// Byte offset of 16-byte chunk c (dims 8c..8c+7) of latent row r in a tile.
-__device__ __forceinline__ int lat_off(int r, int c) { return r * kLatRow + ((c ^ lat_swz(r)) << 4); }
+// Byte offset of latent row r in a tile, and of its 16-byte chunk c (dims
+// 8c..8c+7); the 16-byte shift of rows 8..15 of every 16 stays inside the
+// row's 32 bytes of padding.
+__device__ __forceinline__ int lat_row(int r) { return r * kLatRow + (((r >> 3) & 1) << 4); }
+__device__ __forceinline__ int lat_off(int r, int c) { return lat_row(r) + (c << 4); }
+// Rope chunk c of token t sits in slot c ^ rope_key(t).
+__device__ __forceinline__ int rope_key(int t) { return (t >> 1) & 7; }
 
 // Source of tokens outside the segment: a row of zeros, so that masked
 // positions hold finite values (0 * NaN would poison the PV product).
@@ -136,12 +143,12 @@ __device__ __forceinline__ void issue_one_bf16(const AttnArgs& a, const unsigned
     const int32_t sp = __builtin_amdgcn_readlane(pg.lat, j);
     const unsigned char* src = token_src<kTokBytesBf16>(a, pool, sp, tb + row, hi, zero);
     // slot `lane` of the row holds chunk lane ^ swz(row)
-    dma16(src + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
+    dma16(src + 16 * lane, dst + lat_row(row));
   } else {
     const int jj = j - 16;
     const int u = lane >> 3;                // token within the 8-token group
-    const int chunk = (lane & 7) ^ u;       // slot (lane & 7) holds chunk ^ u
     const int row = 16 * wave + 8 * jj + u;
+    const int chunk = (lane & 7) ^ rope_key(row);   // slot (lane & 7) holds chunk ^ key
     const unsigned char* src =
         token_src<kTokBytesBf16>(a, pool, jj ? pg.rope1 : pg.rope0, tb + row, hi, zero);
     dma16(src + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
@@ -179,12 +186,12 @@ __device__ __forceinline__ void issue_slice(const SliceSrc& v, const unsigned ch
   if (j < 16) {
     const int row = 16 * wave + j;
     const unsigned char* src = j < v.nvalid ? v.base + j * kTokBytesBf16 : zero;
-    dma16(src + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
+    dma16(src + 16 * lane, dst + lat_row(row));
   } else {
     const int jj = j - 16;
     const int u = lane >> 3;
-    const int chunk = (lane & 7) ^ u;
     const int t = 8 * jj + u;                // token within the slice
+    const int chunk = (lane & 7) ^ rope_key(16 * wave + t);
     const unsigned char* src = t < v.nvalid ? v.base + t * kTokBytesBf16 : zero;
     dma16(src + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
   }
@@ -286,13 +293,13 @@ __device__ __forceinline__ void issue_q_tile(const AttnArgs& a, const WorkUnit& 
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int row = 16 * wave + j;
-    dma16(src_of(row) + 16 * (lane ^ lat_swz(row)), dst + row * kLatRow);
+    dma16(src_of(row) + 16 * lane, dst + lat_row(row));
   }
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const int uu = lane >> 3;
-    const int chunk = (lane & 7) ^ uu;
     const int row = 16 * wave + 8 * jj + uu;
+    const int chunk = (lane & 7) ^ rope_key(row);
     dma16(src_of(row) + 2 * kVDim + 16 * chunk, dst + kLatBytes + (16 * wave + 8 * jj) * kRopeRow);
   }
 }
@@ -376,7 +383,7 @@ __device__ __forceinline__ bf16x8 k_fragment(const unsigned char* tile, int tok,
     return *reinterpret_cast<const bf16x8*>(tile + lat_off(tok, 2 * k + h));
   const int chunk = 2 * (k - kLatQSteps) + h;
   return *reinterpret_cast<const bf16x8*>(tile + kLatBytes + tok * kRopeRow +
-                                          16 * (chunk ^ (tok & 7)));
+                                          16 * (chunk ^ rope_key(tok)));
 }
 
 // Q fragments (B operand of S^T = K Q^T) of this lane's row from the staged Q
@@ -394,7 +401,7 @@ __device__ __forceinline__ void read_q(const unsigned char* qtile, int g, int la
     const unsigned char* p =
         k < kLatQSteps ? qtile + lat_off(row, 2 * k + h)
                        : qtile + kLatBytes + row * kRopeRow +
-                             16 * ((2 * (k - kLatQSteps) + h) ^ (row & 7));
+                             16 * ((2 * (k - kLatQSteps) + h) ^ rope_key(row));
     const uint32_t addr = (uint32_t)(uintptr_t)(const lds_void*)p;
     asm volatile("ds_read_b128 %0, %1" : "=a"(qf[k]) : "v"(addr));
   }

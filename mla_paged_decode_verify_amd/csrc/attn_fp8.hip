@@ -120,8 +120,10 @@ __device__ __forceinline__ void write_chunk(const F8Codes& cd, int j, unsigned c
     // latent: chunks cpos/8, cpos/8 + 1 of the row; rope: swizzled slots
     const int cc = (cpos - kVDim) / 8;
     const bool lat = cpos < kVDim;
-    const int d0 = lat ? lat_off(row, cpos / 8) : kLatBytes + row * kRopeRow + 16 * (cc ^ (row & 7));
-    const int d1 = lat ? d0 + 16 : kLatBytes + row * kRopeRow + 16 * ((cc + 1) ^ (row & 7));
+    const int d0 =
+        lat ? lat_off(row, cpos / 8) : kLatBytes + row * kRopeRow + 16 * (cc ^ rope_key(row));
+    const int d1 =
+        lat ? d0 + 16 : kLatBytes + row * kRopeRow + 16 * ((cc + 1) ^ rope_key(row));
     *reinterpret_cast<uint4*>(buf + d0) = w0;
     *reinterpret_cast<uint4*>(buf + d1) = w1;
   }

@@ -7,8 +7,8 @@ the workload's own, measured fastest): shards -- the attention kernel runs one
 workgroup per (shard, split-K segment, row block) unit, normalises each unit's
 result and writes it as bf16 output + natural-log LSE, and the merge is one
 LSE merge over the W * nseg units; persistent -- one workgroup per compute
-unit on equal shares of all tiles (bf16 KV; groups cut between workgroups are
-combined in the kernel), then the LSE merge over the W shards; split -- fp32
+unit on equal shares of all tiles (groups cut between workgroups are combined
+in the kernel), then the LSE merge over the W shards; split -- fp32
 segment partials, then the segment merge and the shard merge. The KV cache is
 rotated over several copies (more than the 256 MB Infinity Cache holds) so
 that no step re-reads the previous step's KV from cache. Timed steps launch
@@ -48,12 +48,12 @@ def parse():
     ap.add_argument("--workload", default="verify_dcp8")
     ap.add_argument("--nseg", type=int, default=None)
     ap.add_argument("--path", choices=["split", "shards", "persistent"], default=None,
-                    help="default: the workload's route (persistent for long_context_dcp8 "
-                         "and ragged_mixed, shards otherwise). shards: attn_shard (every (shard, segment) unit normalised, bf16 "
+                    help="default: the workload's route (persistent for fp8_verify_dcp4, "
+                         "long_context_dcp8 and ragged_mixed, shards otherwise). shards: attn_shard (every (shard, segment) unit normalised, bf16 "
                          "+ LSE) -> shard_merge over the W * nseg units; split: attn fp32 "
                          "partials -> lse_merge (segment merge, then shard merge); "
                          "persistent: attn_persistent (one workgroup per compute unit on "
-                         "equal shares of all tiles, bf16 KV, one segment) -> shard_merge")
+                         "equal shares of all tiles, one segment) -> shard_merge")
     ap.add_argument("--ctas", type=int, default=0,
                     help="persistent path: workgroups (0: one per compute unit)")
     ap.add_argument("--kv-copies", type=int, default=0,
@@ -204,8 +204,8 @@ def main():
     f32 = dict(dtype=torch.float32, device="cuda")
     workspace = None
     if path == "persistent":
-        if nseg != 1 or inp["kv_dtype"] != "bf16":
-            raise SystemExit("the persistent path takes bf16 KV and one segment")
+        if nseg != 1:
+            raise SystemExit("the persistent path takes one segment")
         workspace = torch.zeros(mla.mla_verify_attn_persistent_workspace_bytes(
             inp["N"], W, H, dev["max_qlen"], args.ctas), dtype=torch.uint8, device="cuda")
     if path == "split":

@@ -293,8 +293,7 @@ mla_status_t mla_verify_attn_shard(const void* q, const void* kv,
  * workgroup computes the schedule itself from row_lens and q_start; no extra
  * launch and no host synchronisation.
  *
- *   q .. max_qlen: as for mla_verify_attn_shard; kv_dtype must be
- *              MLA_KV_BF16 (fp8 caches: MLA_ERR_UNSUPPORTED)
+ *   q .. max_qlen: as for mla_verify_attn_shard (bf16, e4m3fn or e5m2 KV)
  *   ctas       workgroups, >= 1; 0 = the current device's compute-unit count
  *   workspace  device, 256-byte aligned, at least
  *              mla_verify_attn_persistent_workspace_bytes(N, W, H, max_qlen,

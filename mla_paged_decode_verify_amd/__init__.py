@@ -409,7 +409,7 @@ def mla_verify_forward_shards(dev, *, nseg=1, plan=None, shards=None, out=None, 
     output + LSE) -> one LSE merge over the W * nseg units, for the same dict
     as mla_verify_forward. ``shards`` may pass (shard_out, shard_lse) buffers.
     persistent: the attention runs on the balanced persistent schedule
-    (mla_verify_attn_persistent; nseg must be 1, bf16 KV), with ``ctas``
+    (mla_verify_attn_persistent; nseg must be 1), with ``ctas``
     workgroups and an optional zeroed ``workspace``.
     Returns a dict with the plan, shard_out, shard_lse, out and lse."""
     if plan is None:

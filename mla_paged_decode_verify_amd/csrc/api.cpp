@@ -319,7 +319,6 @@ mla_status_t mla_verify_attn_persistent(const void* q, const void* kv, int64_t n
                                     kv_scale, sm_scale, row_lens, page_table, pt_width, q_start,
                                     N, R, H, W, max_qlen, 1, a, fp8);
   if (st != MLA_OK) return st;
-  if (fp8) return fail(MLA_ERR_UNSUPPORTED, "%s: bf16 KV caches only", fn);
   if (!shard_out || !shard_lse || !workspace)
     return fail(MLA_ERR_INVALID, "%s: null tensor argument", fn);
   if (!aligned16(shard_out))
@@ -354,7 +353,7 @@ mla_status_t mla_verify_attn_persistent(const void* q, const void* kv, int64_t n
   p.slots = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
                                      persist_counter_bytes(groups));
   p.ctas = ctas;
-  return hip_status(mla::launch_attn_persist(a, p, (hipStream_t)stream), fn);
+  return hip_status(mla::launch_attn_persist(a, p, fp8, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

@@ -36,7 +36,7 @@
 // order -- the same operations whichever piece comes last, so the result does
 // not depend on timing -- then stores the group's rows like a whole group.
 // No workgroup ever waits for another, so every dispatch order completes.
-#include "attn_common.h"
+#include "attn_fp8_tile.h"
 
 namespace mla {
 namespace {
@@ -54,6 +54,7 @@ struct Sched {
   int wsum[8];
   int first_rank, n;
   int lo, hi, total, v;      // this workgroup's range of tiles, the tile total, its index
+  int gang;                  // workgroups per gang: the gcd of the requests' row-block counts
   int cut[2][5];             // g, P, L, qs, Q of the first and last cut item
   int combine[2];
 };
@@ -81,6 +82,29 @@ __device__ __forceinline__ GroupId group_id(const AttnArgs& a, int gg) {
   return id;
 }
 
+// A gang-group: the (request i, gang mbg, shard r) of the schedule; gang mbg
+// is row blocks mbg * gang .. mbg * gang + gang - 1 of the request.
+__device__ __forceinline__ GroupId gang_group_id(const AttnArgs& a, int gg, int ngang) {
+  GroupId id;
+  id.i = gg / (ngang * a.W);
+  const int rem = gg - id.i * ngang * a.W;
+  id.mb = rem / a.W;                        // the gang, not yet the row block
+  id.r = rem - id.mb * a.W;
+  return id;
+}
+// Row blocks of a request with Q rows (at most the grid's mblocks).
+__device__ __forceinline__ int blocks_of(const AttnArgs& a, int Q) {
+  return min((Q * a.H + kAttnRows - 1) / kAttnRows, a.mblocks);
+}
+__device__ __forceinline__ int gcd_int(int x, int y) {
+  while (y != 0) {
+    const int t = x % y;
+    x = y;
+    y = t;
+  }
+  return x;
+}
+
 __device__ __forceinline__ int tiles_of(int L) { return (L + kTile - 1) / kTile; }
 // First tile of workgroup v's range, and the workgroup whose range holds tile t.
 __device__ __forceinline__ int range_lo(int v, int total, int C) {
@@ -95,8 +119,8 @@ __device__ __forceinline__ int range_of(int t, int total, int C) {
 // between the first and the last piece are not all pieces).
 // Slot of the piece of a group starting at tile P in workgroup w: 2w for the
 // workgroup's first item, 2w + 1 for its last.
-__device__ __forceinline__ int slot_of(int w, int P, int total, int C) {
-  return 2 * w + (P > range_lo(w, total, C) ? 1 : 0);
+__device__ __forceinline__ int slot_of(int w, int P, int total, int Cg, int gang) {
+  return 2 * w + (P > range_lo(w / gang, total, Cg) ? 1 : 0);
 }
 
 // Unit of tiles [t0, t1) of group gg.
@@ -154,11 +178,14 @@ __device__ inline void scan2(int x, int y, int* wsum, int tid, int& px, int& py,
   }
 }
 
-// Reads every group's length and fills sc with the items that meet tiles
-// [pos, hi) (at most kMaxItems of them, sc.n). The first call (first set)
-// also sets this workgroup's range [pos, hi). Returns the tile total T.
-__device__ int collect(const AttnArgs& a, Sched& sc, int G, int C, int v, bool first, int& pos,
-                       int& hi, int tid) {
+// Reads every gang-group's length and fills sc with the items that meet
+// tiles [pos, hi) (at most kMaxItems of them, sc.n). The first call (first
+// set) also sets this workgroup's range [pos, hi): the range of its gang,
+// q = v / gang, among the Cg = C / gang gang ranges (none if q >= Cg).
+// Returns the tile total T.
+__device__ int collect(const AttnArgs& a, Sched& sc, int G, int C, int v, int gang, bool first,
+                       int& pos, int& hi, int tid) {
+  const int ngang = (a.mblocks + gang - 1) / gang;
   const int k = (G + kThreads - 1) / kThreads;   // <= kRegGroups
   const int base = tid * k;
   int T[kRegGroups], L[kRegGroups], qs[kRegGroups], Q[kRegGroups];
@@ -168,22 +195,21 @@ __device__ int collect(const AttnArgs& a, Sched& sc, int G, int C, int v, bool f
     qs[j] = 0;
     Q[j] = 0;
     if (j < k && gg < G) {
-      const int i = gg / (a.mblocks * a.W);
+      const int i = gg / (ngang * a.W);
       qs[j] = a.q_start[i];
       Q[j] = a.q_start[i + 1] - qs[j];
     }
   }
-  bool ok[kRegGroups];
 #pragma unroll
   for (int j = 0; j < kRegGroups; ++j) {
     const int gg = base + j;
     T[j] = 0;
     L[j] = 0;
-    ok[j] = false;
     if (j < k && gg < G) {
-      const GroupId id = group_id(a, gg);
-      ok[j] = !(qs[j] < 0 || Q[j] <= 0 || qs[j] + Q[j] > a.R) && id.mb * kAttnRows < Q[j] * a.H;
-      if (ok[j]) {
+      const GroupId id = gang_group_id(a, gg, ngang);
+      const bool ok =
+          !(qs[j] < 0 || Q[j] <= 0 || qs[j] + Q[j] > a.R) && id.mb * gang < blocks_of(a, Q[j]);
+      if (ok) {
         const int Lg = a.row_lens[(int64_t)id.r * a.R + qs[j] + Q[j] - 1];
         L[j] = (int)max((int64_t)0, min((int64_t)Lg, (int64_t)a.pt_width * a.page_size));
         T[j] = tiles_of(L[j]);
@@ -199,8 +225,9 @@ __device__ int collect(const AttnArgs& a, Sched& sc, int G, int C, int v, bool f
   int tpre, npre, total, ntot;
   scan2(tsum, nsum, sc.wsum, tid, tpre, npre, total, ntot);
   if (first) {
-    pos = range_lo(v, total, C);
-    hi = range_lo(v + 1, total, C);
+    const int Cg = C / gang, q = v / gang;
+    pos = q < Cg ? range_lo(q, total, Cg) : 0;
+    hi = q < Cg ? range_lo(q + 1, total, Cg) : 0;
     if (tid == 0) {
       sc.lo = pos;
       sc.hi = hi;
@@ -259,6 +286,26 @@ __device__ __forceinline__ void write_slot(float* slots, int slot, const WaveSta
   b[32 * 64] = make_float4(st.m_ref, st.m_true, st.l_part, 0.f);
 }
 
+// The gang width: the gcd of the well-formed requests' row-block counts, so
+// that every gang of that many workgroups has a row block of each request
+// it meets (1 when there is no request, or when it exceeds the workgroups).
+__device__ int gang_width(const AttnArgs& a, int* wsum, int tid, int C) {
+  int x = 0;
+  for (int i = tid; i < a.N; i += kThreads) {
+    const int qs = a.q_start[i], Q = a.q_start[i + 1] - qs;
+    if (!(qs < 0 || Q <= 0 || qs + Q > a.R)) x = gcd_int(x, blocks_of(a, Q));
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) x = gcd_int(x, __shfl_xor(x, d));
+  if ((tid & 63) == 0) wsum[tid >> 6] = x;
+  lds_barrier();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r = gcd_int(r, wsum[w]);
+  lds_barrier();                            // wsum is the scan's scratch next
+  return (r < 1 || r > C) ? 1 : r;
+}
+
 // End of a whole group inside the tile loop: the normalised form of
 // store_partials written straight from the accumulators (each lane stores its
 // row's 4-dim runs, 8 bytes each), so no tile buffer is needed for staging
@@ -301,7 +348,8 @@ __device__ __forceinline__ void store_rows_direct(const AttnArgs& a, const WorkU
   }
 }
 
-template <bool SLICE>
+// KV: 0 bf16, 1 e4m3fn codes, 2 e5m2 codes.
+template <bool SLICE, int KV>
 __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, PersistArgs ps) {
   __shared__ __align__(16) unsigned char buf0[kBufBytes];
   __shared__ __align__(16) unsigned char buf1[kBufBytes];
@@ -321,15 +369,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
     sc.combine[0] = 0;
     sc.combine[1] = 0;
   }
+  // Gangs: the row blocks of a request attend over the same tiles, so a gang
+  // of `gang` consecutive workgroups takes one range of the sequence of
+  // (request, gang of row blocks, shard) tiles, each workgroup one row block:
+  // the gang's members read each tile at about the same time, through one
+  // L2. Workgroups are dealt to the 8 XCDs round-robin: consecutive virtual
+  // indices go to one XCD, so a gang -- and the neighbouring ranges, which
+  // share requests (their Q, a cut group's slots) -- mostly share an L2.
+  const int C = ps.ctas;
+  const int gang = rfl(gang_width(a, sc.wsum, tid, C));
+  const int ngang = (a.mblocks + gang - 1) / gang;
+  const int Gs = a.N * ngang * a.W;         // gang-groups
+  const int Cg = C / gang;                  // gang ranges
   {
-    // Workgroups are dealt to the 8 XCDs round-robin: consecutive ranges go
-    // to one XCD, so the pieces of a request (its Q, a cut group's slots)
-    // mostly share that XCD's L2.
-    const int C = ps.ctas;
     const int v = (C % 8 == 0) ? (int)(blockIdx.x % 8) * (C / 8) + (int)(blockIdx.x / 8)
                                : (int)blockIdx.x;
     int pos = 0, hi = 0;
-    collect(a, sc, G, C, v, true, pos, hi, tid);
+    collect(a, sc, Gs, C, v, gang, true, pos, hi, tid);
   }
 
   // groups g = v mod C that are well formed but hold no token to read get the
@@ -362,72 +418,126 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
       // every per-lane address of an item is derived from ln where it is used
       const int ln = cold_lane();
       const int P = rfl(sc.P[j]), L = rfl(sc.L[j]);
-      const int gg = rfl(sc.g[j]);
+      const int vv = rfl(sc.v);
+      const GroupId gid = gang_group_id(a, rfl(sc.g[j]), ngang);
+      // this workgroup's row block of the gang: its group (i, mb, r)
+      const int gg = (gid.i * a.mblocks + gid.mb * gang + vv % gang) * a.W + gid.r;
       const WorkUnit u = item_unit(a, gg, rfl(sc.qs[j]), rfl(sc.Q[j]), L,
                                    max(rfl(sc.lo) - P, 0), min(tiles_of(L), rfl(sc.hi) - P));
       const int lo = u.lo, hi = u.hi;
-      const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kTokBytesBf16;
       const int32_t* pt_row = a.page_table + ((int64_t)u.r * a.R + u.last) * a.pt_width;
+      int mrow, hi_row;
+      bool row_ok;
+      const bool idle = u.m0 + 32 * g >= u.M;
+      WaveState st;
+      bf16x8 qf[kQSteps];
+      int32_t vpg = 0;
 
       // ---- Q through the second buffer, then the first tile into the first
       // (once every wave is done with the buffers: the last item's staged rows)
       lds_barrier();
       issue_q_tile(a, u, buf1, wave, ln, zero);
-      int32_t vpg = 0;
-      Bf16Pages pg;
-      if constexpr (SLICE) {
-        vpg = slice_pages(a, pt_row, lo, hi, wave, ln);
-        const SliceSrc v0 = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, 0), lo + 16 * wave, hi);
+      if constexpr (KV == 0) {
+        const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kTokBytesBf16;
+        Bf16Pages pg;
+        if constexpr (SLICE) {
+          vpg = slice_pages(a, pt_row, lo, hi, wave, ln);
+          const SliceSrc v0 =
+              slice_src(a, pool, __builtin_amdgcn_readlane(vpg, 0), lo + 16 * wave, hi);
 #pragma unroll
-        for (int k = 0; k < 18; ++k) issue_slice(v0, zero, buf0, wave, ln, k);
-      } else {
-        pg.fetch(a, pt_row, lo, hi, wave, ln);
-        issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, ln, zero);
-      }
-      if (first_batch && j == 0) do_jobs();
-      int mrow, hi_row;
-      bool row_ok;
-      lane_row(a, u, g, ln, mrow, hi_row, row_ok);
-      const bool idle = u.m0 + 32 * g >= u.M;
-      WaveState st;
-      state_init(st);
-      MLA_WAIT_VMCNT(0);
-      lds_barrier();
-      bf16x8 qf[kQSteps];
-      read_q(buf1, g, ln, qf);
-
-      auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
-        const bool more = tb + kTile < hi;
+          for (int k = 0; k < 18; ++k) issue_slice(v0, zero, buf0, wave, ln, k);
+        } else {
+          pg.fetch(a, pt_row, lo, hi, wave, ln);
+          issue_tile_bf16(a, pool, pg, lo, hi, buf0, wave, ln, zero);
+        }
+        if (first_batch && j == 0) do_jobs();
+        lane_row(a, u, g, ln, mrow, hi_row, row_ok);
+        state_init(st);
         MLA_WAIT_VMCNT(0);
         lds_barrier();
-        SliceSrc v{zero, 0};
-        if constexpr (SLICE) {
-          if (more) {
-            const int nk = kt + 1;
-            if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, ln);
-            v = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile + 16 * wave, hi);
-          }
-        } else {
-          if (more) {
-            pg.fetch(a, pt_row, tb + kTile, hi, wave, ln);
-            issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, ln, zero);
-          }
-        }
-        auto issue = [&](int k) {
+        read_q(buf1, g, ln, qf);
+
+        // one tile: wait until `cur` holds it, stream the next one into `nxt`
+        // during the QK product, compute on `cur`
+        auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
+          const bool more = tb + kTile < hi;
+          MLA_WAIT_VMCNT(0);
+          lds_barrier();
+          SliceSrc v{zero, 0};
           if constexpr (SLICE) {
-            if (more && (k & 1) == 0) issue_slice(v, zero, nxt, wave, ln, k >> 1);
+            if (more) {
+              const int nk = kt + 1;
+              if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, ln);
+              v = slice_src(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63),
+                            tb + kTile + 16 * wave, hi);
+            }
+          } else {
+            if (more) {
+              pg.fetch(a, pt_row, tb + kTile, hi, wave, ln);
+              issue_tile_bf16(a, pool, pg, tb + kTile, hi, nxt, wave, ln, zero);
+            }
           }
+          auto issue = [&](int k) {
+            if constexpr (SLICE) {
+              if (more && (k & 1) == 0) issue_slice(v, zero, nxt, wave, ln, k >> 1);
+            }
+          };
+          if (idle)
+            idle_tile(issue);
+          else
+            compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, ln, issue);
         };
-        if (idle)
-          idle_tile(issue);
-        else
-          compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, ln, issue);
-      };
-      int kt = 0;
-      for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
-        step(buf0, buf1, tb, kt);
-        if (tb + kTile >= hi) break;
-        step(buf1, buf0, tb + kTile, kt + 1);
+        int kt = 0;
+        for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
+          step(buf0, buf1, tb, kt);
+          if (tb + kTile >= hi) break;
+          step(buf1, buf0, tb + kTile, kt + 1);
+        }
+      } else {
+        // fp8 codes: the next tile's codes go into registers during the
+        // current tile and are widened into the other buffer after it
+        constexpr bool E5M2 = KV == 2;
+        const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kHeadDim;
+        F8Codes cd;
+        if constexpr (SLICE) {
+          vpg = f8_slice_pages(a, pt_row, lo, hi, wave, ln);
+          load_codes_slice(cd, a, pool, __builtin_amdgcn_readlane(vpg, 0), lo, hi, wave, ln);
+        } else {
+          load_codes_pages(cd, a, pool, pt_row, lo, hi, wave, ln, zero);
+        }
+        if (first_batch && j == 0) do_jobs();
+        lane_row(a, u, g, ln, mrow, hi_row, row_ok);
+        state_init(st);
+        write_codes<E5M2>(cd, buf0, wave, ln);
+        MLA_WAIT_VMCNT(0);
+        lds_barrier();
+        read_q(buf1, g, ln, qf);
+
+        auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
+          const bool more = tb + kTile < hi;
+          lds_barrier();                    // `cur` is written; `nxt` is no longer read
+          if (more) {
+            if constexpr (SLICE) {
+              const int nk = kt + 1;
+              if ((nk & 63) == 0) vpg = f8_slice_pages(a, pt_row, lo + nk * kTile, hi, wave, ln);
+              load_codes_slice(cd, a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile,
+                               hi, wave, ln);
+            } else {
+              load_codes_pages(cd, a, pool, pt_row, tb + kTile, hi, wave, ln, zero);
+            }
+          }
+          if (idle)
+            idle_tile([](int) {});
+          else
+            compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, ln, [](int) {});
+          if (more) write_codes<E5M2>(cd, nxt, wave, ln);
+        };
+        int kt = 0;
+        for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
+          step(buf0, buf1, tb, kt);
+          if (tb + kTile >= hi) break;
+          step(buf1, buf0, tb + kTile, kt + 1);
+        }
       }
 
       // ---- a whole group is stored; a cut piece writes its state to its
@@ -436,7 +546,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
         store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, ln);
         continue;
       }
-      write_slot(ps.slots, slot_of(rfl(sc.v), P, rfl(sc.total), ps.ctas), st, wave, ln);
+      write_slot(ps.slots, slot_of(vv, P, rfl(sc.total), Cg, gang), st, wave, ln);
       if (tid == 0 && ncut < 2) {
         int* f = sc.cut[ncut];
         f[0] = gg;
@@ -454,7 +564,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
     if (end >= rfl(sc.hi)) break;
     int pos = end, hi_v = rfl(sc.hi);
     __syncthreads();
-    collect(a, sc, G, ps.ctas, rfl(sc.v), false, pos, hi_v, tid);
+    collect(a, sc, Gs, C, rfl(sc.v), gang, false, pos, hi_v, tid);
   }
 
   // ---- arrivals of this workgroup's cut pieces, counted once all its work is
@@ -462,7 +572,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
   // before the barrier, and the release fence then makes this compute unit's
   // stores visible device-wide before the counters move); the pieces that
   // arrive last combine their group
-  const int total = rfl(sc.total), C = ps.ctas;
+  const int total = rfl(sc.total), vlane = rfl(sc.v) % gang;
   if (ncut > 0) {
     MLA_WAIT_VMCNT(0);
     __syncthreads();
@@ -475,7 +585,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
           __hip_atomic_fetch_add(ps.counters + f[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int end = f[1] + tiles_of(f[2]);
       int np = 0;
-      for (int t = f[1]; t < end; t = range_lo(range_of(t, total, C) + 1, total, C)) ++np;
+      for (int t = f[1]; t < end; t = range_lo(range_of(t, total, Cg) + 1, total, Cg)) ++np;
       if (old == np - 1) {
         __hip_atomic_store(ps.counters + f[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sc.combine[k] = 1;
@@ -494,13 +604,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
     const size_t lane_off = (size_t)wave * kSlotVecs * 64 + lane;
     auto slot_ptr = [&](int w) {
       return reinterpret_cast<const float4*>(
-                 ps.slots + (size_t)slot_of(w, Pc, total, C) * (kPersistSlotBytes / 4)) +
+                 ps.slots + (size_t)slot_of(w, Pc, total, Cg, gang) * (kPersistSlotBytes / 4)) +
              lane_off;
     };
     float M = kNegInf, mt = kNegInf;
     for (int t = Pc; t < end;) {
-      const int w = range_of(t, total, C);
-      t = range_lo(w + 1, total, C);
+      const int qq = range_of(t, total, Cg);
+      const int w = qq * gang + vlane;
+      t = range_lo(qq + 1, total, Cg);
       const float4 s = slot_ptr(w)[32 * 64];
       M = fmaxf(M, s.x);
       mt = fmaxf(mt, s.y);
@@ -509,8 +620,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
     state_init(ms);
     float l = 0.f;
     for (int t = Pc; t < end;) {
-      const int w = range_of(t, total, C);
-      t = range_lo(w + 1, total, C);
+      const int qq = range_of(t, total, Cg);
+      const int w = qq * gang + vlane;
+      t = range_lo(qq + 1, total, Cg);
       const float4* b = slot_ptr(w);
       const float4 s = b[32 * 64];
       const float wgt = s.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s.x - M);
@@ -540,12 +652,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
 
 }  // namespace
 
-hipError_t launch_attn_persist(const AttnArgs& a, const PersistArgs& p, hipStream_t s) {
+hipError_t launch_attn_persist(const AttnArgs& a, const PersistArgs& p, bool fp8, hipStream_t s) {
   if (p.ctas <= 0) return hipErrorInvalidConfiguration;
-  if (a.page_size >= 16)
-    attn_persist_kernel<true><<<(unsigned)p.ctas, kThreads, 0, s>>>(a, p);
-  else
-    attn_persist_kernel<false><<<(unsigned)p.ctas, kThreads, 0, s>>>(a, p);
+  const unsigned n = (unsigned)p.ctas;
+  const bool slice = a.page_size >= 16;
+  if (!fp8) {
+    if (slice) attn_persist_kernel<true, 0><<<n, kThreads, 0, s>>>(a, p);
+    else attn_persist_kernel<false, 0><<<n, kThreads, 0, s>>>(a, p);
+  } else if (!a.e5m2) {
+    if (slice) attn_persist_kernel<true, 1><<<n, kThreads, 0, s>>>(a, p);
+    else attn_persist_kernel<false, 1><<<n, kThreads, 0, s>>>(a, p);
+  } else {
+    if (slice) attn_persist_kernel<true, 2><<<n, kThreads, 0, s>>>(a, p);
+    else attn_persist_kernel<false, 2><<<n, kThreads, 0, s>>>(a, p);
+  }
   return hipGetLastError();
 }
 

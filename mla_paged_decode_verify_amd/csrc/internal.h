@@ -103,7 +103,7 @@ hipError_t static_scratch(void** ptr);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_attn_fp8(const AttnArgs& a, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_persist(const AttnArgs& a, const PersistArgs& p, hipStream_t s);
+hipError_t launch_attn_persist(const AttnArgs& a, const PersistArgs& p, bool fp8, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 

@@ -265,7 +265,7 @@ def test_persistent_workspace_bytes():
 
 
 @pytest.mark.parametrize("over,code,msg", [
-    (dict(kv_dtype=1), _lib.MLA_ERR_UNSUPPORTED, "bf16"),
+    (dict(kv_dtype=7), _lib.MLA_ERR_UNSUPPORTED, "kv_dtype"),
     (dict(workspace=None), _lib.MLA_ERR_INVALID, "null"),
     (dict(workspace=FAKE + 16), _lib.MLA_ERR_INVALID, "256-byte"),
     (dict(workspace_bytes=1000), _lib.MLA_ERR_INVALID, "workspace of 1000 bytes"),

@@ -46,6 +46,12 @@ SMALL_BF16 = {
     "heads12_q7_m84": small_spec(N=3, H=12, qlen=7, W=2, seq_range=(70, 260)),
     "ragged_q": dict(N=5, H=8, qlen_range=(1, 8), seq_range=(8, 200), block_size=32, W=3,
                      kv_dtype="bf16", nseg=1),
+    # gangs of 4: row blocks {4, 8, 12} per request
+    "heads128_q246": dict(N=3, H=128, qlens=[2, 4, 6], seq_lens=[300, 90, 700], block_size=64,
+                          W=2, kv_dtype="bf16", nseg=1),
+    # gangs of 2 with an odd max block count: {2, 4} of 4
+    "heads64_q24": dict(N=4, H=64, qlens=[2, 4, 2, 4], seq_lens=[150, 400, 64, 230],
+                        block_size=32, W=3, kv_dtype="bf16", nseg=1),
     "w_gt_s": dict(N=4, H=4, qlens=[1, 2, 3, 4], seq_lens=[1, 3, 5, 4], block_size=16, W=8,
                    kv_dtype="bf16", nseg=1),
     "q_equals_s": dict(N=2, H=16, qlens=[7, 1], seq_lens=[7, 1], block_size=16, W=2,
@@ -54,34 +60,45 @@ SMALL_BF16 = {
 
 
 def schedule_model(row_lens, q_start, W, H, max_qlen, pt_width, page_size, ctas):
-    """Pieces of every group under the schedule the kernel computes: groups
-    (i, mb, r) in that order, T_g = ceil(min(longest row, table) / 64) tiles,
-    workgroup v taking tiles [v T / C, (v + 1) T / C)."""
+    """Pieces of every group (i, mb, r) under the schedule the kernel
+    computes: gangs of g = gcd(row blocks of every request) workgroups (1 if
+    that exceeds ctas); gang-groups (i, gang, r) in that order with
+    T = ceil(min(longest row, table) / 64) tiles; gang range q of the
+    ctas // g takes tiles [q T / Cg, (q + 1) T / Cg), one row block per member."""
     N = len(q_start) - 1
     mblocks = -(-max_qlen * H // 64)
+    nb = [min(-(-(int(q_start[i + 1]) - int(q_start[i])) * H // 64), mblocks) for i in range(N)]
+    gang = 0
+    for x in nb:
+        gang = math.gcd(gang, x)
+    if gang < 1 or gang > ctas:
+        gang = 1
+    ngang = -(-mblocks // gang)
+    Cg = ctas // gang
     groups, T = [], []
     for i in range(N):
         qs, qe = int(q_start[i]), int(q_start[i + 1])
-        for mb in range(mblocks):
+        for mg in range(ngang):
             for r in range(W):
-                ok = mb * 64 < (qe - qs) * H
+                ok = mg * gang < nb[i]
                 L = min(int(row_lens[r, qe - 1]), pt_width * page_size) if ok else 0
-                groups.append((i, mb, r))
+                groups.append((i, mg, r))
                 T.append(-(-L // 64))
     total = sum(T)
     pieces = {}
     P = 0
-    for gid, t in zip(groups, T):
+    for (i, mg, r), t in zip(groups, T):
         if t > 0:
-            # workgroups whose (non-empty) ranges meet tiles [P, P + t)
+            # gang ranges whose (non-empty) tile ranges meet tiles [P, P + t)
             n, x = 0, P
             while x < P + t:
-                w = ((x + 1) * ctas - 1) // total
-                x = (w + 1) * total // ctas
+                q = ((x + 1) * Cg - 1) // total
+                x = (q + 1) * total // Cg
                 n += 1
-            pieces[gid] = n
+            for b in range(gang):
+                pieces[(i, mg * gang + b, r)] = n
         P += t
-    return pieces, total
+    return pieces, total, gang
 
 
 def run_persistent(inp, ctas, workspace=None, max_qlen=None):
@@ -116,11 +133,11 @@ def test_persistent_small(name, ctas):
     dev, res = run_persistent(inp, ctas)
     plan = res["plan"]
     row_lens = plan["row_lens"].cpu().numpy()
-    pieces, total = schedule_model(row_lens, inp["q_start"], inp["W"], inp["H"],
-                                   int(np.max(inp["qlens"])), plan["page_table"].shape[2],
-                                   plan["page_size"], ctas)
+    pieces, total, gang = schedule_model(row_lens, inp["q_start"], inp["W"], inp["H"],
+                                         int(np.max(inp["qlens"])), plan["page_table"].shape[2],
+                                         plan["page_size"], ctas)
     ncut = sum(1 for p in pieces.values() if p > 1)
-    say(f"  {total} tiles, {len(pieces)} groups with tiles, {ncut} cut "
+    say(f"  {total} tiles, gang {gang}, {len(pieces)} groups with tiles, {ncut} cut "
         f"(most pieces {max(pieces.values(), default=0)})")
     g_so = res["shard_out"].float().cpu().numpy().astype(np.float64)
     g_sl = res["shard_lse"].cpu().numpy().astype(np.float64)
@@ -212,8 +229,68 @@ def test_persistent_understated_max_qlen_gives_nan():
     assert max_err(lse[covered], lse_ref[covered]) <= TOL_LSE
 
 
-def test_persistent_rejects_fp8():
-    inp = wl.make_workload(small_spec(kv_dtype="fp8_e4m3"), seed=1)
-    dev = wl.to_device(inp)
-    with pytest.raises(mla.MlaError):
-        mla.mla_verify_forward_shards(dev, persistent=True)
+SMALL_FP8 = {
+    "fp8_w4": small_spec(W=4, kv_dtype="fp8_e4m3", qlen=7, H=12, seq_range=(100, 600)),
+    "fp8_odd_block_p4": small_spec(W=3, block_size=12, kv_dtype="fp8_e4m3", qlen=3, H=8,
+                                   seq_range=(40, 300)),
+    "e5m2_w4": small_spec(W=4, kv_dtype="fp8_e5m2", qlen=7, H=12, seq_range=(100, 600)),
+    "fp8_q_equals_s": dict(N=2, H=12, qlens=[7, 1], seq_lens=[7, 1], block_size=16, W=2,
+                           kv_dtype="fp8_e4m3", nseg=1),
+}
+
+
+@pytest.mark.parametrize("ctas", [1, 5, 64, 256])
+@pytest.mark.parametrize("name", sorted(SMALL_FP8))
+def test_persistent_fp8_small(name, ctas):
+    """fp8 caches (e4m3fn, e5m2; sub-pages of 64 and of 4 tokens) on the
+    persistent schedule: uncut groups equal the unit kernel's bits, every
+    per-shard result and the final out / lse match the oracle."""
+    inp = wl.make_workload(dict(SMALL_FP8[name]), seed=1)
+    say(f"persistent fp8 case {name} ctas={ctas} S={inp['seq_lens'].tolist()}")
+    dev, res = run_persistent(inp, ctas)
+    plan = res["plan"]
+    pieces, total, gang = schedule_model(plan["row_lens"].cpu().numpy(), inp["q_start"],
+                                         inp["W"], inp["H"], int(np.max(inp["qlens"])),
+                                         plan["page_table"].shape[2], plan["page_size"], ctas)
+    say(f"  {total} tiles, gang {gang}, {sum(1 for p in pieces.values() if p > 1)} cut groups")
+    g_so = res["shard_out"].float().cpu().numpy().astype(np.float64)
+    g_sl = res["shard_lse"].cpu().numpy().astype(np.float64)
+    assert not np.any(np.isnan(g_so)) and not np.any(np.isnan(g_sl))
+    so1, sl1 = mla.mla_verify_attn_shard(dev["q"], dev["kv"], plan["row_lens"],
+                                         plan["page_table"], dev["q_start"],
+                                         page_size=plan["page_size"], max_qlen=dev["max_qlen"],
+                                         sm_scale=dev["sm_scale"], kv_scale=dev["kv_scale"],
+                                         nseg=1)
+    torch.cuda.synchronize()
+    so1 = so1.float().cpu().numpy().astype(np.float64)
+    sl1 = sl1.cpu().numpy().astype(np.float64)
+    for (i, mb, r), p in pieces.items():
+        if p == 1:
+            rows, heads = _rows_of_group(inp, i, mb)
+            assert np.array_equal(g_so[r, rows, heads], so1[r, rows, heads])
+            assert np.array_equal(g_sl[r, rows, heads], sl1[r, rows, heads])
+    so, sl, sa, _ = oracle_shard_results(inp, oracle_plan(inp), 1, want_parts=False)
+    check_out(g_so, so, inp["kv_dtype"], "persistent fp8 per-shard", sa)
+    assert max_err(g_sl, sl) <= TOL_LSE
+    out_ref, lse_ref = orc.verify_reference(inp)
+    g_out = res["out"].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g_out))
+    check_out(g_out, out_ref, inp["kv_dtype"], "persistent fp8 out (bf16 hand-off)",
+              weighted_abs_v(inp), handoff=True)
+    assert max_err(res["lse"].cpu().numpy(), lse_ref) <= TOL_LSE
+
+
+def test_persistent_fp8_named_workload():
+    """fp8_verify_dcp4 at full size on one workgroup per compute unit, every
+    request: out / lse against the oracle."""
+    inp = named_workload("fp8_verify_dcp4")
+    _, res = run_persistent(inp, 0)
+    g_out = res["out"].float().cpu().numpy().astype(np.float64)
+    g_lse = res["lse"].cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g_out)) and np.all(np.isfinite(g_lse))
+    out_ref, lse_ref = orc.verify_reference(inp)
+    eo, _ = check_out(g_out, out_ref, "fp8_e4m3", "fp8_verify_dcp4 persistent out",
+                      weighted_abs_v(inp), handoff=True)
+    el = max_err(g_lse, lse_ref)
+    say(f"persistent fp8_verify_dcp4: max|dout|={eo:.3e} max|dlse|={el:.3e}")
+    assert el <= TOL_LSE

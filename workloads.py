@@ -42,9 +42,11 @@ CONFIGS = {
     "verify_dcp8": dict(N=32, H=16, qlen=4, seq_range=(1024, 8192),
                         block_size=64, W=8, kv_dtype="bf16", nseg=1),
     # batch 64, 12 heads, qlen 7, seq_len U[4096, 32768], fp8 KV, 4 shards
-    # (split-K segments: the count measured fastest here; the config leaves it open)
+    # (split-K segments: the count measured fastest for the unit-per-workgroup
+    # kernel; the config leaves it open. "path": the route measured fastest)
     "fp8_verify_dcp4": dict(N=64, H=12, qlen=7, seq_range=(4096, 32768),
-                            block_size=64, W=4, kv_dtype="fp8_e4m3", nseg=2),
+                            block_size=64, W=4, kv_dtype="fp8_e4m3", nseg=2,
+                            path="persistent"),
     # batch 16, 16 heads, qlen 4, seq_len 132000, 8 shards, 16 segments
     # (nseg: the pages' split for the unit-per-workgroup kernel; "path": the
     # route measured fastest, the persistent kernel, whose balanced schedule

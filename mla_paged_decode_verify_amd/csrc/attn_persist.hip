@@ -1,41 +1,44 @@
-// Balanced persistent attention over a bf16 KV cache, normalised form: each
-// shard's output of a row, normalised and rounded to bf16, with its
+// Balanced persistent attention (bf16, e4m3fn or e5m2 KV), normalised form:
+// each shard's output of a row, normalised and rounded to bf16, with its
 // natural-log LSE, as source r of the shard merge (the results of
 // mla_verify_attn_shard with one segment).
 //
 // The work of a launch -- the KV tiles of every (request i, row block mb,
-// shard r) group, groups in (i, mb, r) order and each group's tiles in token
-// order -- is one sequence of T tiles, cut into C contiguous ranges:
-// workgroup v takes tiles [floor(v T / C), floor((v + 1) T / C)). With one
-// workgroup per compute unit every unit streams for about the same time,
-// whatever the spread of the groups' lengths; a workgroup per group would
-// end with the longest groups running alone. (The pages' ASM decode runs a
-// persistent kernel on per-launch work metadata as well: vLLM PR #51011
-// digest, Implementation breakdown item 3. The split used here is this
-// library's own.)
+// shard r) group, each group's tiles in token order -- is one sequence of T
+// tiles, cut into contiguous ranges of floor or ceil of T / C tiles, one per
+// workgroup (C workgroups, one per compute unit). Every unit then streams for
+// about the same time whatever the spread of the groups' lengths; a
+// workgroup per group would end with the longest groups running alone. (The
+// pages' ASM decode runs a persistent kernel on per-launch work metadata as
+// well: vLLM PR #51011 digest, Implementation breakdown item 3. The split
+// used here is this library's own.)
+//
+// Gangs: the row blocks of a request attend over the same tiles. With g the
+// gcd of the requests' row-block counts, the sequence is over (request, gang
+// of g row blocks, shard) and cut into C / g ranges; the g workgroups of a
+// gang take the same range, one row block each, so they read each tile at
+// about the same time and share it through one L2.
 //
 // Each workgroup computes the schedule itself when it starts: every thread
-// reads the lengths of up to kRegGroups consecutive groups (q_start, then the
-// group's longest row length -- the reads a workgroup per group makes
-// anyway), and a workgroup-wide prefix sum over their tile counts gives every
-// group's first tile P_g. The groups that meet the workgroup's range are its
-// items, computed back to back through the tile pipeline of the bf16 kernel
-// (two LDS buffers, direct HBM -> LDS loads): the last tile of an item
-// streams in the first tile of the next one, whose sub-page entries and row
-// lengths were fetched when the item began; Q is reloaded only when the next
-// item belongs to another (request, row block).
+// reads the lengths of up to kRegGroups consecutive gang-groups (q_start,
+// then the group's longest row length), and a workgroup-wide prefix sum over
+// their tile counts gives every gang-group's first tile P. The gang-groups
+// that meet the workgroup's range are its items; each item runs like one work
+// unit of the unit-per-workgroup kernels (Q and the first tile loaded, the
+// same tile loop and per-tile computation), so a group inside one range gets
+// the unit kernels' results bit for bit.
 //
-// A group inside one range is finished there (its rows normalised and
-// stored). A group cut between workgroups has one piece per workgroup it
-// meets; each piece writes its partial state (O relative to its reference
-// exponent, the reference, the running maximum and the exp2 sum, per lane in
-// the accumulator layout) to a slot of its own and then, after a device-scope
-// release fence, adds one to the group's arrival counter (a vector atomic).
-// The piece that arrives last (it reads pieces - 1) resets the counter, takes
-// a device-scope acquire fence and combines all pieces' states in piece
-// order -- the same operations whichever piece comes last, so the result does
-// not depend on timing -- then stores the group's rows like a whole group.
-// No workgroup ever waits for another, so every dispatch order completes.
+// A group cut between ranges has one piece per workgroup it meets; each piece
+// writes its partial state (O relative to its reference exponent, the
+// reference, the running maximum and the exp2 sum, per lane in the
+// accumulator layout) to a slot of its own. When all its items are done, a
+// workgroup takes one device-scope release fence and adds one to each of its
+// cut groups' arrival counters (vector atomics). The piece that arrives last
+// (it reads pieces - 1) resets the counter, takes a device-scope acquire fence
+// and combines all pieces' states in piece order -- the same operations
+// whichever piece comes last, so the result does not depend on timing -- then
+// stores the group's rows like a whole group. No workgroup ever waits for
+// another, so every dispatch order completes.
 #include "attn_fp8_tile.h"
 
 namespace mla {
@@ -54,15 +57,14 @@ struct Sched {
   int wsum[8];
   int first_rank, n;
   int lo, hi, total, v;      // this workgroup's range of tiles, the tile total, its index
-  int gang;                  // workgroups per gang: the gcd of the requests' row-block counts
   int cut[2][5];             // g, P, L, qs, Q of the first and last cut item
   int combine[2];
 };
 
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
-// This lane's index, opaque to the optimiser: the item-switch code derives its
-// per-lane addresses from it where it runs, instead of the compiler hoisting
-// them out of the tile loop and holding them in registers across it.
+// This lane's index, opaque to the optimiser: each item derives its per-lane
+// addresses from it, so the compiler cannot hoist them out of the item loop
+// and hold them in registers across every item's tile loop.
 __device__ __forceinline__ int cold_lane() {
   int x = (int)(threadIdx.x & 63);
   asm volatile("" : "+v"(x));
@@ -306,11 +308,10 @@ __device__ int gang_width(const AttnArgs& a, int* wsum, int tid, int C) {
   return (r < 1 || r > C) ? 1 : r;
 }
 
-// End of a whole group inside the tile loop: the normalised form of
-// store_partials written straight from the accumulators (each lane stores its
-// row's 4-dim runs, 8 bytes each), so no tile buffer is needed for staging
-// and the next item's first tile can already be streaming into the other one.
-// Same fp32 operations as store_partials, so the same results.
+// The normalised form of store_partials written straight from the
+// accumulators (each lane stores its row's 4-dim runs, 8 bytes each), with no
+// LDS staging: the combination of a cut group's pieces. Same fp32 operations
+// as store_partials, so an uncut group would get the same results.
 __device__ __forceinline__ void store_rows_direct(const AttnArgs& a, const WorkUnit& u,
                                                   const WaveState& st, RowExchange& rx, int mrow,
                                                   bool row_ok, int g, int c, int lane) {

@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA verify attention KV GB/s (% of HBM peak) + verify rows/sec at 1 GPU"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = 2500.0          # dense bf16 (the fp8 path widens to bf16 before its MFMAs)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense, by the MFMA operand type
 
 
 def parse():
@@ -75,8 +75,8 @@ def parse():
 
 # sources of the attention kernel that runs a workload, by its KV dtype and path
 ATTN_SOURCES = {"bf16": ["attn_common.h", "attn_bf16.hip", "internal.h"],
-                "fp8": ["attn_common.h", "attn_fp8.hip", "internal.h"],
-                "persistent": ["attn_common.h", "attn_persist.hip", "internal.h"]}
+                "fp8": ["attn_common.h", "attn_f8mma.h", "attn_fp8.hip", "internal.h"],
+                "persistent": ["attn_common.h", "attn_f8mma.h", "attn_persist.hip", "internal.h"]}
 ATTN_KERNELS = {"bf16": "attn_bf16_kernel", "fp8": "attn_fp8_kernel",
                 "persistent": "attn_persist_kernel"}
 
@@ -135,8 +135,9 @@ def stored_traffic(workload, path="shards"):
 
 
 def stored_mfma_flops(workload, path="shards"):
-    """Executed MFMA flops per attention launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
-    512) from the committed counter summary, or None."""
+    """Executed MFMA flops per attention launch ((SQ_INSTS_VALU_MFMA_MOPS_BF16 +
+    SQ_INSTS_VALU_MFMA_MOPS_F8) x 512) from the committed counter summary, or
+    None."""
     kv = _stored(workload, path, "mfma")
     try:
         return float(kv["executed_mfma_flops_per_launch"])
@@ -351,6 +352,8 @@ def main():
     ms_step = wall * 1e3 / args.steps
     achieved = kv_bytes / (attn_launch_ms * 1e-3) / 1e9
     mfma_flops = stored_mfma_flops(args.workload, path)
+    # bf16 KV runs on bf16 MFMAs, fp8 KV on the fp8 ones (both kernels)
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16" if inp["kv_dtype"] == "bf16" else "fp8"]
     res = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -358,8 +361,9 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8e4m3-kv/bf16",
-                  "fp8_e5m2": "fp8e5m2-kv/bf16"}[inp["kv_dtype"]],
+        # fp8 KV: fp8 MFMAs, KV codes against Q and P as e4m3fn term pairs
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8e4m3",
+                  "fp8_e5m2": "fp8e5m2-kv/fp8e4m3"}[inp["kv_dtype"]],
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp["N"], "heads": H,
                    "qlen": int(np.max(inp["qlens"])), "rows": R, "shards": W,
@@ -390,8 +394,8 @@ def main():
         "mfma": None if mfma_flops is None else {
             "executed_flops_per_launch": mfma_flops,
             "achieved_tflops": round(mfma_flops / (attn_launch_ms * 1e-3) / 1e12, 1),
-            "peak_tflops": MFMA_PEAK_TFLOPS,
-            "util": round(mfma_flops / (attn_launch_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)},
+            "peak_tflops": mfma_peak,
+            "util": round(mfma_flops / (attn_launch_ms * 1e-3) / 1e12 / mfma_peak, 4)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

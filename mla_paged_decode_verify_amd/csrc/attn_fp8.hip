@@ -1,18 +1,15 @@
 // Split-K segmented MLA attention partials, fp8 KV cache (OCP e4m3fn or e5m2
-// codes).
+// codes), on the fp8 matrix cores.
 //
-// The quantities computed, the work decomposition and the per-tile
-// computation are those of attn_common.h, on the same double-buffered bf16
-// tiles as the bf16 kernel. Specific to this kernel:
-//  * The codes of the next 64-token tile (576 B per token) are fetched into
-//    registers with ordinary vector loads while the current tile is computed
-//    (each wave: its 16 tokens, nine 16-byte loads per lane), then widened
-//    exactly to bf16 (every e4m3fn and every e5m2 value is a bf16 value) and
-//    written into the other tile buffer in the latent / rope layout of
-//    attn_common.h: no separate widening pass, no extra barrier, and the LDS
-//    holds no staging copy of the codes.
-//  * The fp8 scale is folded into the score scale and into the output.
-#include "attn_fp8_tile.h"
+// The quantities computed and the work decomposition are those of
+// attn_common.h; the per-tile computation is compute_tile_f8 (attn_f8mma.h):
+// the codes go from HBM into LDS as they are, by direct loads, and feed the
+// scaled fp8 MFMAs with Q and P as two e4m3fn terms each. An fp8 tile is half
+// a bf16 one, so the two tile buffers hold four: tile k uses slot k mod 4 and
+// the loads of tile k + 2 go out during tile k. Q is staged (bf16) in the
+// second buffer first and split into its terms before tiles 2 and 3 land
+// there. The fp8 scale is folded into the score scale and into the output.
+#include "attn_f8mma.h"
 
 namespace mla {
 namespace {
@@ -49,58 +46,79 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
     store_empty(a, u, wave, lane);
     return;
   }
+  const int ntiles = (hi - lo + kTile - 1) / kTile;
 
-  // ---- Q (through the second tile buffer, as in the bf16 kernel) and the
-  // first tile's codes, widened into the first buffer
+  // all nine loads of this wave for tile k (slice path: k < 64)
+  auto issue_all = [&](int k) {
+    unsigned char* dst = f8_slot(buf0, buf1, k & 3);
+    const int tb = lo + k * kTile;
+    if constexpr (SLICE) {
+      const __amdgpu_buffer_rsrc_t r =
+          f8_slice_rsrc(a, pool, __builtin_amdgcn_readlane(vpg, k & 63), tb + 16 * wave, hi);
+#pragma unroll
+      for (int j = 0; j < kF8Dma; ++j) issue_f8_slice(r, dst, wave, lane, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kF8Dma; ++j)
+        issue_f8_pages(a, pool, pt_row, tb, hi, dst, wave, lane, j, zero);
+    }
+  };
+
+  // ---- Q (bf16, through the second buffer) and the first two tiles
   issue_q_tile(a, u, buf1, wave, lane, zero);
-  F8Codes cd;
   if constexpr (SLICE) {
-    if (u.s != 0) vpg = f8_slice_pages(a, pt_row, lo, hi, wave, lane);
-    load_codes_slice(cd, a, pool, __builtin_amdgcn_readlane(vpg, 0), lo, hi, wave, lane);
-  } else {
-    load_codes_pages(cd, a, pool, pt_row, lo, hi, wave, lane, zero);
+    if (u.s != 0) vpg = slice_pages(a, pt_row, lo, hi, wave, lane);
   }
+  issue_all(0);
+  if (ntiles > 1) issue_all(1);
   int mrow, hi_row;
   bool row_ok;
   lane_row(a, u, g, lane, mrow, hi_row, row_ok);
   const bool idle = u.m0 + 32 * g >= u.M;   // no row of this row group in the block
   WaveState st;
   state_init(st);
-  write_codes<E5M2>(cd, buf0, wave, lane);
-  MLA_WAIT_VMCNT(0);                        // the direct loads of Q
+  if (ntiles > 1)
+    MLA_WAIT_VMCNT(kF8Dma);                 // Q and tile 0 have landed
+  else
+    MLA_WAIT_VMCNT(0);
   lds_barrier();
-  bf16x8 qf[kQSteps];
-  read_q(buf1, g, lane, qf);
+  QF8 q;
+  read_q_f8(buf1, g, lane, q);
+  lds_barrier();                            // the second buffer is free for tiles 2, 3
 
-  // One tile (index kt from the segment start): wait until `cur` holds it,
-  // fetch the next tile's codes, compute on `cur`, then widen the codes into
-  // `nxt` (their loads had the whole computation to land; measured faster
-  // than widening them piecewise during the PV product, 437 vs 456 us on
-  // the fp8 verify workload).
-  auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
-    const bool more = tb + kTile < hi;
-    lds_barrier();                          // `cur` is written; `nxt` is no longer read
-    if (more) {
+  for (int k = 0; k < ntiles; ++k) {
+    const int tb = lo + k * kTile;
+    if (k > 0) {
+      if (k + 1 < ntiles)
+        MLA_WAIT_VMCNT(kF8Dma);             // tile k has landed (tile k + 1 may not have) ...
+      else
+        MLA_WAIT_VMCNT(0);
+      lds_barrier();                        // ... for every wave; slot (k + 2) mod 4 is free
+    }
+    const bool more2 = k + 2 < ntiles;
+    unsigned char* nxt = f8_slot(buf0, buf1, (k + 2) & 3);
+    __amdgpu_buffer_rsrc_t rs = f8_slice_rsrc(a, pool, -1, 0, 0);
+    if (more2) {
       if constexpr (SLICE) {
-        const int nk = kt + 1;
-        if ((nk & 63) == 0) vpg = f8_slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
-        load_codes_slice(cd, a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile, hi,
-                         wave, lane);
+        const int nk = k + 2;
+        if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
+        rs = f8_slice_rsrc(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63),
+                           lo + nk * kTile + 16 * wave, hi);
       } else {
-        load_codes_pages(cd, a, pool, pt_row, tb + kTile, hi, wave, lane, zero);
+        issue_all(k + 2);                   // table entries first: one wait, then the loads
       }
     }
+    // one load per QK K-step (slice path)
+    auto issue = [&](int s) {
+      if constexpr (SLICE) {
+        if (more2) issue_f8_slice(rs, nxt, wave, lane, s);
+      }
+    };
+    const unsigned char* cur = f8_slot(buf0, buf1, k & 3);
     if (idle)
-      idle_tile([](int) {});
+      idle_tile_f8(issue);
     else
-      compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, lane, [](int) {});
-    if (more) write_codes<E5M2>(cd, nxt, wave, lane);
-  };
-  int kt = 0;
-  for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
-    step(buf0, buf1, tb, kt);
-    if (tb + kTile >= hi) break;
-    step(buf1, buf0, tb + kTile, kt + 1);
+      compute_tile_f8<E5M2>(cur, &px, q, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
   }
 
   store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);

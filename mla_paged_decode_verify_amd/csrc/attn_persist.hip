@@ -39,7 +39,7 @@
 // whichever piece comes last, so the result does not depend on timing -- then
 // stores the group's rows like a whole group. No workgroup ever waits for
 // another, so every dispatch order completes.
-#include "attn_fp8_tile.h"
+#include "attn_f8mma.h"
 
 namespace mla {
 namespace {
@@ -495,49 +495,71 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
           step(buf1, buf0, tb + kTile, kt + 1);
         }
       } else {
-        // fp8 codes: the next tile's codes go into registers during the
-        // current tile and are widened into the other buffer after it
+        // fp8 codes, straight into LDS and onto the fp8 matrix cores
+        // (compute_tile_f8): four tile slots in the two buffers, tile k + 2
+        // loading during tile k; Q (staged in the second buffer) is split
+        // into its e4m3fn terms before tiles 2 and 3 land there
         constexpr bool E5M2 = KV == 2;
         const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kHeadDim;
-        F8Codes cd;
-        if constexpr (SLICE) {
-          vpg = f8_slice_pages(a, pt_row, lo, hi, wave, ln);
-          load_codes_slice(cd, a, pool, __builtin_amdgcn_readlane(vpg, 0), lo, hi, wave, ln);
-        } else {
-          load_codes_pages(cd, a, pool, pt_row, lo, hi, wave, ln, zero);
-        }
+        const int ntiles = (hi - lo + kTile - 1) / kTile;
+        auto issue_all = [&](int k) {       // slice path: k < 64
+          unsigned char* dst = f8_slot(buf0, buf1, k & 3);
+          const int tb = lo + k * kTile;
+          if constexpr (SLICE) {
+            const __amdgpu_buffer_rsrc_t r =
+                f8_slice_rsrc(a, pool, __builtin_amdgcn_readlane(vpg, k & 63), tb + 16 * wave, hi);
+#pragma unroll
+            for (int jj = 0; jj < kF8Dma; ++jj) issue_f8_slice(r, dst, wave, ln, jj);
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < kF8Dma; ++jj)
+              issue_f8_pages(a, pool, pt_row, tb, hi, dst, wave, ln, jj, zero);
+          }
+        };
+        if constexpr (SLICE) vpg = slice_pages(a, pt_row, lo, hi, wave, ln);
+        issue_all(0);
+        if (ntiles > 1) issue_all(1);
         if (first_batch && j == 0) do_jobs();
         lane_row(a, u, g, ln, mrow, hi_row, row_ok);
         state_init(st);
-        write_codes<E5M2>(cd, buf0, wave, ln);
         MLA_WAIT_VMCNT(0);
         lds_barrier();
-        read_q(buf1, g, ln, qf);
+        QF8 q;
+        read_q_f8(buf1, g, ln, q);
+        lds_barrier();                      // the second buffer is free for tiles 2, 3
 
-        auto step = [&](const unsigned char* cur, unsigned char* nxt, int tb, int kt) {
-          const bool more = tb + kTile < hi;
-          lds_barrier();                    // `cur` is written; `nxt` is no longer read
-          if (more) {
+        for (int k = 0; k < ntiles; ++k) {
+          const int tb = lo + k * kTile;
+          if (k > 0) {
+            if (k + 1 < ntiles)
+              MLA_WAIT_VMCNT(kF8Dma);       // tile k has landed (tile k + 1 may not have) ...
+            else
+              MLA_WAIT_VMCNT(0);
+            lds_barrier();                  // ... for every wave; slot (k + 2) mod 4 is free
+          }
+          const bool more2 = k + 2 < ntiles;
+          unsigned char* nxt = f8_slot(buf0, buf1, (k + 2) & 3);
+          __amdgpu_buffer_rsrc_t rs = f8_slice_rsrc(a, pool, -1, 0, 0);
+          if (more2) {
             if constexpr (SLICE) {
-              const int nk = kt + 1;
-              if ((nk & 63) == 0) vpg = f8_slice_pages(a, pt_row, lo + nk * kTile, hi, wave, ln);
-              load_codes_slice(cd, a, pool, __builtin_amdgcn_readlane(vpg, nk & 63), tb + kTile,
-                               hi, wave, ln);
+              const int nk = k + 2;
+              if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, ln);
+              rs = f8_slice_rsrc(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63),
+                                 lo + nk * kTile + 16 * wave, hi);
             } else {
-              load_codes_pages(cd, a, pool, pt_row, tb + kTile, hi, wave, ln, zero);
+              issue_all(k + 2);
             }
           }
+          auto issue = [&](int s) {
+            if constexpr (SLICE) {
+              if (more2) issue_f8_slice(rs, nxt, wave, ln, s);
+            }
+          };
+          const unsigned char* cur = f8_slot(buf0, buf1, k & 3);
           if (idle)
-            idle_tile([](int) {});
+            idle_tile_f8(issue);
           else
-            compute_tile(cur, &px, qf, st, tb, hi_row, a.qk_scale_log2, g, c, ln, [](int) {});
-          if (more) write_codes<E5M2>(cd, nxt, wave, ln);
-        };
-        int kt = 0;
-        for (int tb = lo; tb < hi; tb += 2 * kTile, kt += 2) {
-          step(buf0, buf1, tb, kt);
-          if (tb + kTile >= hi) break;
-          step(buf1, buf0, tb + kTile, kt + 1);
+            compute_tile_f8<E5M2>(cur, &px, q, st, tb, hi_row, a.qk_scale_log2, g, c, ln, issue);
         }
       }
 

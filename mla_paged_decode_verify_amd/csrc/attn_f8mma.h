@@ -230,136 +230,184 @@ __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const 
                                                           0, scale_b);
 }
 
-// Scores, softmax and PV for one 64-token fp8 tile in `tile` (LDS).
-// `issue(s)` is called once per QK K-step (s = 0..8), so that the loads of a
-// later tile can be spread over the MFMA work.
-template <bool E5M2, class Issue>
-__device__ __forceinline__ void compute_tile_f8(const unsigned char* __restrict__ tile,
-                                                PExchange* __restrict__ px, const QF8& q,
-                                                WaveState& st, int tb, int hi_row,
-                                                float qk_scale_log2, int g, int c, int lane,
-                                                Issue&& issue) {
-  const int h = lane >> 5;
-  const int n32 = lane & 31;
+// K fragment (A operand of S^T = K Q^T) of K-step s: lane l reads token
+// 32c + l % 32 of `tile`, dims 64s + 32h .. + 31 (two 16-byte chunks).
+__device__ __forceinline__ i32x8 kfrag_f8(const unsigned char* tile, int tok, int h, int s) {
+  const uint4 x0 = *reinterpret_cast<const uint4*>(tile + f8_off(tok, 4 * s + 2 * h));
+  const uint4 x1 = *reinterpret_cast<const uint4*>(tile + f8_off(tok, 4 * s + 2 * h + 1));
+  return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+               (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
 
-  // ---- S^T[32 tokens x 32 rows]: lane l reads token 32c + l % 32, dims
-  // 64s + 32h .. + 31 (two 16-byte chunks), one K-step ahead of its MFMAs
-  const int tok = 32 * c + n32;
-  auto kfrag = [&](int s) -> i32x8 {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(tile + f8_off(tok, 4 * s + 2 * h));
-    const uint4 x1 = *reinterpret_cast<const uint4*>(tile + f8_off(tok, 4 * s + 2 * h + 1));
-    return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                 (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-  };
-  f32x16 sacc = f32x16{};
+// V^T fragment (A operand of O^T += V^T P^T) of output tile t: dims
+// 256c + 32t + l % 32 over the 64 tokens in the B operand's order -- bytes
+// 0..15 the wave's own tokens 32c + 8(j/4) + 4h + j%4, bytes 16..31 the
+// partner's (32(c^1) + ...). Transposed 8-bit read r covers bytes 8r .. 8r+7:
+// in each 16-lane group, lane 2k + b points at 8 dims (b: the upper 8 of the
+// group's 16) of token T_k and hands out one dim of 8 tokens.
+__device__ __forceinline__ i32x8 vfrag_f8(const unsigned char* tile, int c, int lane, int t) {
+  const int h = lane >> 5;
+  const int G = (lane >> 4) & 1;
+  const int kk = (lane & 15) >> 1;
+  const int b8 = lane & 1;
+  i32x2 r4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int half = r < 2 ? c : (c ^ 1);
+    const int T = 32 * half + 16 * (r & 1) + 8 * (kk >> 2) + 4 * h + (kk & 3);
+    r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2*)(tile + f8_off(T, 16 * c + 2 * t + G) + 8 * b8));
+  }
+  return i32x8{r4[0][0], r4[0][1], r4[1][0], r4[1][1], r4[2][0], r4[2][1], r4[3][0], r4[3][1]};
+}
+
+// S^T[32 tokens x 32 rows] of one tile (the first of a segment): 9 K-steps,
+// hi and lo terms of Q into one accumulator.
+template <bool E5M2>
+__device__ __forceinline__ void qk_f8(const unsigned char* __restrict__ tile, const QF8& q,
+                                      f32x16& sacc, int c, int lane) {
+  const int tok = 32 * c + (lane & 31), h = lane >> 5;
+  sacc = f32x16{};
   i32x8 kr[2];
-  kr[0] = kfrag(0);
+  kr[0] = kfrag_f8(tile, tok, h, 0);
 #pragma unroll
   for (int s = 0; s < kF8Steps; ++s) {
-    if (s + 1 < kF8Steps) kr[(s + 1) & 1] = kfrag(s + 1);
-    issue(s);
+    if (s + 1 < kF8Steps) kr[(s + 1) & 1] = kfrag_f8(tile, tok, h, s + 1);
     __builtin_amdgcn_sched_barrier(0);
     sacc = mfma_f8<E5M2>(kr[s & 1], q.hi[s], sacc, q.sc_hi);
     sacc = mfma_f8<E5M2>(kr[s & 1], q.lo[s], sacc, q.sc_lo);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
 
-  // ---- mask, maximum (both waves of the row group), lazy reference: as in
-  // the bf16 tile
-  if (__builtin_amdgcn_ballot_w64(tb + kTile > hi_row) != 0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int t = tb + 32 * c + 8 * (j >> 2) + 4 * h + (j & 3);
-      if (t >= hi_row) sacc[j] = kNegInf;
-    }
-  }
-  float m = sacc[0];
-#pragma unroll
-  for (int j = 1; j < 16; ++j) m = fmaxf(m, sacc[j]);
-  {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-  }
-  if (h == 0) px->mx[g][c][n32] = m;
+// One step of the tile pipeline: softmax and PV of tile `cur`, whose scores
+// `sacc` the previous step computed, interleaved with the QK product of the
+// next tile `nxt` (its scores replace `sacc`). The matrix cores work on the
+// next tile's QK while the wave computes this tile's maxima and weights
+// between its MFMAs, then on this tile's PV. On a segment's last tile `nxt`
+// is any tile slot: its scores are not used. `issue(s)` is called once per
+// QK K-step (s = 0..8), so that the loads of a later tile can be spread over
+// the MFMA work.
+template <bool E5M2, class Issue>
+__device__ __forceinline__ void step_f8(const unsigned char* __restrict__ cur,
+                                        const unsigned char* __restrict__ nxt, f32x16& sacc,
+                                        PExchange* __restrict__ px, const QF8& q, WaveState& st,
+                                        int tb, int hi_row, float qk_scale_log2, int g, int c,
+                                        int lane, Issue&& issue) {
+  const int h = lane >> 5;
+  const int n32 = lane & 31;
+  const int tok = 32 * c + n32;
 
-  // ---- V^T fragments: output tile t (dims 256c + 32t + l % 32) over the 64
-  // tokens in the B operand's order -- bytes 0..15 the wave's own tokens
-  // 32c + 8(j/4) + 4h + j%4, bytes 16..31 the partner's (32(c^1) + ...).
-  // Transposed 8-bit read r covers bytes 8r .. 8r + 7: in each 16-lane group,
-  // lane 2k + b points at 8 dims (b selects the upper 8 of the group's 16) of
-  // token T_k and hands out one dim of 8 tokens.
-  const int G = (lane >> 4) & 1;
-  const int kk = (lane & 15) >> 1;
-  const int b8 = lane & 1;
-  auto vread = [&](int t) -> i32x8 {
-    i32x2 r4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int half = r < 2 ? c : (c ^ 1);
-      const int T = 32 * half + 16 * (r & 1) + 8 * (kk >> 2) + 4 * h + (kk & 3);
-      const int chunk = 16 * c + 2 * t + G;
-      r4[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2*)(tile + f8_off(T, chunk) + 8 * b8));
-    }
-    return i32x8{r4[0][0], r4[0][1], r4[1][0], r4[1][1], r4[2][0], r4[2][1], r4[3][0], r4[3][1]};
-  };
-  i32x8 vr[2];
-  vr[0] = vread(0);
-
-  lds_barrier();
-  m = fmaxf(m, px->mx[g][c ^ 1][n32]) * qk_scale_log2;
-  st.m_true = fmaxf(st.m_true, m);
-  const bool refresh = m > st.m_ref + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(refresh) != 0) {
-    const float alpha = refresh ? __builtin_amdgcn_exp2f(st.m_ref - m) : 1.f;
-    st.l_part *= alpha;
-#pragma unroll
-    for (int t = 0; t < kOTiles; ++t) st.o[t] *= alpha;
-    st.m_ref = refresh ? m : st.m_ref;
-  }
-
-  // ---- P of this wave's tokens as hi / lo e4m3fn terms; published for the
-  // partner
-  const float m_use = st.m_ref == kNegInf ? 0.f : st.m_ref;
+  f32x16 sc = sacc;                         // this tile's scores
+  float m = 0.f;
   int ph[4], pl[4];
+  i32x8 bh, bl, v0;
+
+  // ---- this tile's softmax, in pieces placed between the next tile's QK
+  // MFMAs (piece i after MFMA i)
+  auto piece = [&](int i) {
+    if (i == 0) {
+      // mask and maximum (both waves of the row group see the same tile max)
+      if (__builtin_amdgcn_ballot_w64(tb + kTile > hi_row) != 0) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    float x[4];
+        for (int j = 0; j < 16; ++j) {
+          const int t = tb + 32 * c + 8 * (j >> 2) + 4 * h + (j & 3);
+          if (t >= hi_row) sc[j] = kNegInf;
+        }
+      }
+      m = sc[0];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * w + k], qk_scale_log2, -m_use));
-      st.l_part += x[k];
+      for (int j = 1; j < 16; ++j) m = fmaxf(m, sc[j]);
+      auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false,
+                                                false);
+      m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    } else if (i == 1) {
+      if (h == 0) px->mx[g][c][n32] = m;
+      v0 = vfrag_f8(cur, c, lane, 0);
+    } else if (i == 3) {
+      lds_barrier();
+      m = fmaxf(m, px->mx[g][c ^ 1][n32]) * qk_scale_log2;
+      st.m_true = fmaxf(st.m_true, m);
+      // lazily refreshed reference (identical decisions on both waves)
+      const bool refresh = m > st.m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(refresh) != 0) {
+        const float alpha = refresh ? __builtin_amdgcn_exp2f(st.m_ref - m) : 1.f;
+        st.l_part *= alpha;
+#pragma unroll
+        for (int t = 0; t < kOTiles; ++t) st.o[t] *= alpha;
+        st.m_ref = refresh ? m : st.m_ref;
+      }
+    } else if (i >= 4 && i < 8) {
+      // P of this wave's tokens as hi / lo e4m3fn terms, one word each
+      const int w = i - 4;
+      const float m_use = st.m_ref == kNegInf ? 0.f : st.m_ref;
+      float x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // masked: the score is -inf and exp2(-inf) = 0 (m_use is finite)
+        x[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * w + k], qk_scale_log2, -m_use));
+        st.l_part += x[k];
+      }
+      int hw = pk_e4m3(x[0], x[1], 0, false);
+      hw = pk_e4m3(x[2], x[3], hw, true);
+      const f32x2 b0 = unpk_e4m3(hw, false), b1 = unpk_e4m3(hw, true);
+      const float f = (float)(1 << kLoShift);
+      int lw = pk_e4m3((x[0] - b0[0]) * f, (x[1] - b0[1]) * f, 0, false);
+      lw = pk_e4m3((x[2] - b1[0]) * f, (x[3] - b1[1]) * f, lw, true);
+      asm volatile("" : "+v"(hw), "+v"(lw), "+v"(st.l_part));   // keeps the pieces apart
+      ph[w] = hw;
+      pl[w] = lw;
+    } else if (i == 8) {
+      px->p[g][c][0][lane] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+      px->p[g][c][1][lane] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    } else if (i == 11) {
+      lds_barrier();
+      const uint4 oh = px->p[g][c ^ 1][0][lane];
+      const uint4 ol = px->p[g][c ^ 1][1][lane];
+      bh = i32x8{ph[0], ph[1], ph[2], ph[3], (int)oh.x, (int)oh.y, (int)oh.z, (int)oh.w};
+      bl = i32x8{pl[0], pl[1], pl[2], pl[3], (int)ol.x, (int)ol.y, (int)ol.z, (int)ol.w};
     }
-    int hw = pk_e4m3(x[0], x[1], 0, false);
-    hw = pk_e4m3(x[2], x[3], hw, true);
-    const f32x2 b0 = unpk_e4m3(hw, false), b1 = unpk_e4m3(hw, true);
-    const float sc = (float)(1 << kLoShift);
-    int lw = pk_e4m3((x[0] - b0[0]) * sc, (x[1] - b0[1]) * sc, 0, false);
-    lw = pk_e4m3((x[2] - b1[0]) * sc, (x[3] - b1[1]) * sc, lw, true);
-    ph[w] = hw;
-    pl[w] = lw;
+  };
+
+  // ---- the next tile's S^T, with the pieces between its MFMAs
+  f32x16 sn = f32x16{};
+  i32x8 kr[2];
+  kr[0] = kfrag_f8(nxt, tok, h, 0);
+#pragma unroll
+  for (int s = 0; s < kF8Steps; ++s) {
+    if (s + 1 < kF8Steps) kr[(s + 1) & 1] = kfrag_f8(nxt, tok, h, s + 1);
+    issue(s);
+    __builtin_amdgcn_sched_barrier(0);
+    sn = mfma_f8<E5M2>(kr[s & 1], q.hi[s], sn, q.sc_hi);
+    // pinned here: left alone, the compiler sinks the MFMAs, whose results
+    // are used only after the loop, below all the pieces
+    asm volatile("" : "+v"(sn));
+    __builtin_amdgcn_sched_barrier(0);
+    piece(2 * s);
+    __builtin_amdgcn_sched_barrier(0);
+    sn = mfma_f8<E5M2>(kr[s & 1], q.lo[s], sn, q.sc_lo);
+    asm volatile("" : "+v"(sn));
+    __builtin_amdgcn_sched_barrier(0);
+    piece(2 * s + 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  px->p[g][c][0][lane] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-  px->p[g][c][1][lane] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-  lds_barrier();
-  const uint4 oh = px->p[g][c ^ 1][0][lane];
-  const uint4 ol = px->p[g][c ^ 1][1][lane];
-  const i32x8 bh = {ph[0], ph[1], ph[2], ph[3], (int)oh.x, (int)oh.y, (int)oh.z, (int)oh.w};
-  const i32x8 bl = {pl[0], pl[1], pl[2], pl[3], (int)ol.x, (int)ol.y, (int)ol.z, (int)ol.w};
 
   // ---- O^T[256 dims x 32 rows] += V^T[256 x 64 tokens] P^T[64 x 32]
+  i32x8 vr[2];
+  vr[0] = v0;
 #pragma unroll
   for (int t = 0; t < kOTiles; ++t) {
-    if (t + 1 < kOTiles) vr[(t + 1) & 1] = vread(t + 1);
+    if (t + 1 < kOTiles) vr[(t + 1) & 1] = vfrag_f8(cur, c, lane, t + 1);
     __builtin_amdgcn_sched_barrier(0);
     st.o[t] = mfma_f8<E5M2>(vr[t & 1], bh, st.o[t], kE8M0One);
     st.o[t] = mfma_f8<E5M2>(vr[t & 1], bl, st.o[t], kE8M0One - kLoShift);
     __builtin_amdgcn_sched_barrier(0);
   }
+  sacc = sn;
 }
 
 // A tile for a wave whose row group holds no row of the block: its share of
-// a later tile's loads and compute_tile_f8's two barriers.
+// a later tile's loads and step_f8's two barriers.
 template <class Issue>
 __device__ __forceinline__ void idle_tile_f8(Issue&& issue) {
 #pragma unroll

@@ -2,13 +2,15 @@
 // codes), on the fp8 matrix cores.
 //
 // The quantities computed and the work decomposition are those of
-// attn_common.h; the per-tile computation is compute_tile_f8 (attn_f8mma.h):
-// the codes go from HBM into LDS as they are, by direct loads, and feed the
-// scaled fp8 MFMAs with Q and P as two e4m3fn terms each. An fp8 tile is half
-// a bf16 one, so the two tile buffers hold four: tile k uses slot k mod 4 and
-// the loads of tile k + 2 go out during tile k. Q is staged (bf16) in the
-// second buffer first and split into its terms before tiles 2 and 3 land
-// there. The fp8 scale is folded into the score scale and into the output.
+// attn_common.h; the per-tile computation is step_f8 (attn_f8mma.h): the
+// codes go from HBM into LDS as they are, by direct loads, and feed the
+// scaled fp8 MFMAs with Q and P as two e4m3fn terms each; each step runs the
+// softmax and PV of tile k around the QK product of tile k + 1. An fp8 tile
+// is half a bf16 one, so the two tile buffers hold four: tile k uses slot
+// k mod 4 and the loads of tile k + 3 go out during step k. Q is staged
+// (bf16) in the second buffer first and split into its terms before tiles 2
+// and 3 land there. The fp8 scale is folded into the score scale and into the
+// output.
 #include "attn_f8mma.h"
 
 namespace mla {
@@ -85,40 +87,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
   QF8 q;
   read_q_f8(buf1, g, lane, q);
   lds_barrier();                            // the second buffer is free for tiles 2, 3
+  if (ntiles > 2) issue_all(2);
+  f32x16 sacc;
+  if (!idle) qk_f8<E5M2>(f8_slot(buf0, buf1, 0), q, sacc, c, lane);
 
   for (int k = 0; k < ntiles; ++k) {
     const int tb = lo + k * kTile;
-    if (k > 0) {
-      if (k + 1 < ntiles)
-        MLA_WAIT_VMCNT(kF8Dma);             // tile k has landed (tile k + 1 may not have) ...
-      else
-        MLA_WAIT_VMCNT(0);
-      lds_barrier();                        // ... for every wave; slot (k + 2) mod 4 is free
-    }
-    const bool more2 = k + 2 < ntiles;
-    unsigned char* nxt = f8_slot(buf0, buf1, (k + 2) & 3);
+    if (k + 2 < ntiles)
+      MLA_WAIT_VMCNT(kF8Dma);               // tile k + 1 has landed (tile k + 2 may not have) ...
+    else
+      MLA_WAIT_VMCNT(0);
+    lds_barrier();                          // ... for every wave; slot (k + 3) mod 4 is free
+    const bool more3 = k + 3 < ntiles;
+    unsigned char* dst = f8_slot(buf0, buf1, (k + 3) & 3);
     __amdgpu_buffer_rsrc_t rs = f8_slice_rsrc(a, pool, -1, 0, 0);
-    if (more2) {
+    if (more3) {
       if constexpr (SLICE) {
-        const int nk = k + 2;
+        const int nk = k + 3;
         if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, lane);
         rs = f8_slice_rsrc(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63),
                            lo + nk * kTile + 16 * wave, hi);
       } else {
-        issue_all(k + 2);                   // table entries first: one wait, then the loads
+        issue_all(k + 3);                   // table entries first: one wait, then the loads
       }
     }
     // one load per QK K-step (slice path)
     auto issue = [&](int s) {
       if constexpr (SLICE) {
-        if (more2) issue_f8_slice(rs, nxt, wave, lane, s);
+        if (more3) issue_f8_slice(rs, dst, wave, lane, s);
       }
     };
-    const unsigned char* cur = f8_slot(buf0, buf1, k & 3);
     if (idle)
       idle_tile_f8(issue);
     else
-      compute_tile_f8<E5M2>(cur, &px, q, st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
+      step_f8<E5M2>(f8_slot(buf0, buf1, k & 3), f8_slot(buf0, buf1, (k + 1) & 3), sacc, &px, q,
+                    st, tb, hi_row, a.qk_scale_log2, g, c, lane, issue);
   }
 
   store_partials(a, u, st, rx, g == 0 ? buf0 : buf1, mrow, row_ok, g, c, lane);

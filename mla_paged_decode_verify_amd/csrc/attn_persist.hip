@@ -496,9 +496,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
         }
       } else {
         // fp8 codes, straight into LDS and onto the fp8 matrix cores
-        // (compute_tile_f8): four tile slots in the two buffers, tile k + 2
-        // loading during tile k; Q (staged in the second buffer) is split
-        // into its e4m3fn terms before tiles 2 and 3 land there
+        // (step_f8: softmax and PV of tile k around the QK product of tile
+        // k + 1): four tile slots in the two buffers, tile k + 3 loading
+        // during step k; Q (staged in the second buffer) is split into its
+        // e4m3fn terms before tiles 2 and 3 land there
         constexpr bool E5M2 = KV == 2;
         const unsigned char* pool = a.kv + (int64_t)u.r * a.pool_tokens * kHeadDim;
         const int ntiles = (hi - lo + kTile - 1) / kTile;
@@ -527,39 +528,40 @@ __global__ void __launch_bounds__(kThreads, 1) attn_persist_kernel(AttnArgs a, P
         QF8 q;
         read_q_f8(buf1, g, ln, q);
         lds_barrier();                      // the second buffer is free for tiles 2, 3
+        if (ntiles > 2) issue_all(2);
+        f32x16 sacc;
+        if (!idle) qk_f8<E5M2>(f8_slot(buf0, buf1, 0), q, sacc, c, ln);
 
         for (int k = 0; k < ntiles; ++k) {
           const int tb = lo + k * kTile;
-          if (k > 0) {
-            if (k + 1 < ntiles)
-              MLA_WAIT_VMCNT(kF8Dma);       // tile k has landed (tile k + 1 may not have) ...
-            else
-              MLA_WAIT_VMCNT(0);
-            lds_barrier();                  // ... for every wave; slot (k + 2) mod 4 is free
-          }
-          const bool more2 = k + 2 < ntiles;
-          unsigned char* nxt = f8_slot(buf0, buf1, (k + 2) & 3);
+          if (k + 2 < ntiles)
+            MLA_WAIT_VMCNT(kF8Dma);         // tile k + 1 has landed (tile k + 2 may not have) ...
+          else
+            MLA_WAIT_VMCNT(0);
+          lds_barrier();                    // ... for every wave; slot (k + 3) mod 4 is free
+          const bool more3 = k + 3 < ntiles;
+          unsigned char* dst = f8_slot(buf0, buf1, (k + 3) & 3);
           __amdgpu_buffer_rsrc_t rs = f8_slice_rsrc(a, pool, -1, 0, 0);
-          if (more2) {
+          if (more3) {
             if constexpr (SLICE) {
-              const int nk = k + 2;
+              const int nk = k + 3;
               if ((nk & 63) == 0) vpg = slice_pages(a, pt_row, lo + nk * kTile, hi, wave, ln);
               rs = f8_slice_rsrc(a, pool, __builtin_amdgcn_readlane(vpg, nk & 63),
                                  lo + nk * kTile + 16 * wave, hi);
             } else {
-              issue_all(k + 2);
+              issue_all(k + 3);
             }
           }
           auto issue = [&](int s) {
             if constexpr (SLICE) {
-              if (more2) issue_f8_slice(rs, nxt, wave, ln, s);
+              if (more3) issue_f8_slice(rs, dst, wave, ln, s);
             }
           };
-          const unsigned char* cur = f8_slot(buf0, buf1, k & 3);
           if (idle)
             idle_tile_f8(issue);
           else
-            compute_tile_f8<E5M2>(cur, &px, q, st, tb, hi_row, a.qk_scale_log2, g, c, ln, issue);
+            step_f8<E5M2>(f8_slot(buf0, buf1, k & 3), f8_slot(buf0, buf1, (k + 1) & 3), sacc, &px,
+                          q, st, tb, hi_row, a.qk_scale_log2, g, c, ln, issue);
         }
       }
 

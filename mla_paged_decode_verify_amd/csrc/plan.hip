@@ -63,8 +63,13 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   __shared__ int32_t len_lds[kPlanLdsRows];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
+  // the request's first 256 block ids go out with its length and rows (one
+  // round trip less before the checks; entries past its blocks are unused)
+  const int32_t* bt = a.block_table + (int64_t)i * a.max_blocks;
+  const int32_t id0 = tid < a.max_blocks ? bt[tid] : 0;
   const int qs = a.q_start[i], qe = a.q_start[i + 1];
   const int S = a.seq_lens[i];
+  const int q_end = i == 0 ? a.q_start[a.N] : a.R;   // the batch's row count (checked once)
   const int per = a.block_size / a.page_size;   // sub-pages per block
 
   // ---- request checks (uniform), then the block ids it uses (all threads)
@@ -83,11 +88,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
       nb = 0;
     }
   }
-  const int32_t* bt = a.block_table + (int64_t)i * a.max_blocks;
   const bool staged = npages <= kPlanLdsPages;  // uniform
   int bad = 0;
   for (int64_t b = tid; b < nb; b += kPlanThreads) {
-    const int32_t id = bt[b];
+    const int32_t id = b == tid ? id0 : bt[b];
     bad |= (id < 0 || (int64_t)id >= a.num_blocks);
     if (staged)
       for (int j = 0; j < per && b * per + j < npages; ++j) pages_lds[b * per + j] = id * per + j;
@@ -95,7 +99,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(PlanArgs a) {
   if (__syncthreads_or(bad)) bits |= MLA_PLAN_ERR_BLOCKS;
   if (tid == 0 && a.err_flag != nullptr) {
     uint32_t all = bits;
-    if (i == 0 && (a.q_start[0] != 0 || a.q_start[a.N] != a.R)) all |= MLA_PLAN_ERR_ROWS;
+    if (i == 0 && (qs != 0 || q_end != a.R)) all |= MLA_PLAN_ERR_ROWS;
     if (all != 0) atomicOr(a.err_flag, all);
   }
   if (i == 0 && tid == 0 && a.qo_indptr != nullptr) a.qo_indptr[a.R] = a.R;

@@ -206,8 +206,9 @@ mla_status_t mla_verify_two_stage_plan(int32_t N, const int32_t* seq_lens,
  *   kv_scale   fp8 descale (real = code * kv_scale), > 0; ignored for bf16.
  *              fp8 caches run on the fp8 matrix cores: the codes against Q and
  *              the softmax weights, each as two e4m3fn terms (Q exact for a
- *              bf16 input but for elements some 2^17 below its row's largest;
- *              each weight within 2^-8 of itself plus 2^-14)
+ *              bf16 input down to 2^-13 of its row's largest, below that
+ *              within 2^-21 of it; each weight within 2^-8 of itself plus
+ *              2^-14)
  *   sm_scale   softmax scale applied to <q, k> (e.g. 1/sqrt(576)), > 0; the
  *              product sm_scale * kv_scale * log2(e) must be a positive
  *              finite fp32 value, else MLA_ERR_INVALID

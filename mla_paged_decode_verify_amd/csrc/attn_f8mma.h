@@ -8,8 +8,9 @@
 //    element, Q = 2^-a (hi + 2^-4 lo), a per row such that 2^a max|q| lies in
 //    [128, 256). A bf16 value has 8 significant bits and hi keeps the top 4
 //    (nearest even), so the residual needs at most 4 more: lo is exact and
-//    the two terms give q exactly, unless elements some 2^17 below the row's
-//    largest fall into e4m3fn's subnormal range. The per-row factors are
+//    the two terms give q exactly for every element at least 2^-13 of the
+//    row's largest; a smaller one's residual can fall under e4m3fn's
+//    subnormal spacing, an error below 2^-21 of the row's largest. The per-row factors are
 //    the B operand's block scales (E8M0) of the scaled MFMA, so both terms
 //    accumulate into one fp32 accumulator.
 //  * O^T += V^T P^T with V the latent codes and P as two e4m3fn terms,

@@ -294,19 +294,29 @@ def _wrong_row_lens(inp, row_lens, kind):
     return bad
 
 
+@pytest.mark.parametrize("name", ["tiny_decode_q4", "verify_dcp8"])
 @pytest.mark.parametrize("kind", ["subtract_offset", "prefix_only"])
-def test_wrong_row_views_fail_the_bounds_on_the_gpu(kind):
-    """Negative controls on the verify workload: the kernels run with a wrong
-    row view (the correct table still covers every row) and their result
-    must then fail the stated bounds against the oracle somewhere -- the
-    parity checks above would catch either mistake."""
-    inp = named_workload("verify_dcp8")
+def test_wrong_row_views_fail_the_bounds_on_the_gpu(kind, name):
+    """Negative controls on the verify workload and on the tiny-decode one
+    with four verify rows: the kernels run with a wrong row view (the
+    correct table still covers every row) and their result must then fail
+    the stated bounds against the oracle somewhere -- the parity checks
+    above would catch either mistake."""
+    if name == "tiny_decode_q4":
+        inp = wl.make_workload(dict(wl.CONFIGS["tiny_decode"], qlen=4), 0)
+    else:
+        inp = named_workload(name)
     dev = wl.to_device(inp)
     plan = mla.mla_verify_plan(dev["seq_lens"], dev["q_start"], dev["R"], dev["W"],
                                dev["block_table"], dev["num_blocks"], dev["block_size"],
                                dev["max_kv_seq_len"])
     torch.cuda.synchronize()
     bad = _wrong_row_lens(inp, plan["row_lens"].cpu().numpy(), kind)
+    if kind == "subtract_offset" and inp["W"] == 1:
+        # one shard holds every dropped token, so the offset view is the
+        # right one there: the pages' objection needs W > 1
+        assert np.array_equal(bad, plan["row_lens"].cpu().numpy())
+        return
     bad_dev = torch.from_numpy(bad.astype(np.int32)).to("cuda")
     parts = mla.mla_verify_attn(dev["q"], dev["kv"], bad_dev, plan["page_table"],
                                 dev["q_start"], page_size=plan["page_size"],
@@ -319,7 +329,7 @@ def test_wrong_row_views_fail_the_bounds_on_the_gpu(kind):
     dl = np.abs(lse.cpu().numpy() - lse_ref)
     n_out = int((d > TOL_OUT["bf16"]).sum())
     n_lse = int((dl > TOL_LSE).sum())
-    say(f"{kind}: {n_out}/{d.size} out elements over 1e-2 (max {d.max():.4f}), "
+    say(f"{name} {kind}: {n_out}/{d.size} out elements over 1e-2 (max {d.max():.4f}), "
         f"{n_lse}/{dl.size} lse over 1e-3 (max {dl.max():.4f})")
     assert n_out > 0 and n_lse > 0
 

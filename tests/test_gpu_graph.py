@@ -189,14 +189,15 @@ def test_graph_one_segment_route_replays_new_lengths():
         assert torch.equal(shards[1], split["shard_lse"])
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("ctas", [0, 7])
-def test_graph_persistent_route_replays_new_lengths(ctas):
+def test_graph_persistent_route_replays_new_lengths(ctas, kv_dtype):
     """The persistent route (plan -> attn_persistent -> shard_merge) captured
     once with one workspace: its arrival counters are left at zero by every
     launch, so each replay -- lengths changed in place before it, some groups
     cut between workgroups, some shards empty -- equals an eager run of the
     same route on the new lengths bit for bit."""
-    spec = small_spec(N=6, W=4, qlen=3, seq_range=(100, 1500), nseg=1)
+    spec = small_spec(N=6, W=4, qlen=3, seq_range=(100, 1500), nseg=1, kv_dtype=kv_dtype)
     inp = wl.make_workload(spec, seed=21)
     dev = wl.to_device(inp)
     nbytes = mla.mla_verify_attn_persistent_workspace_bytes(inp["N"], inp["W"], inp["H"],
